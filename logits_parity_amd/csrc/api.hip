@@ -1,0 +1,486 @@
+// C ABI of libphi: argument checks, workspace planning and the stream-ordered
+// launch sequence of the prefill forward and of the decode attention.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/phi.h"
+#include "attention.hpp"
+#include "common.hpp"
+#include "decode.hpp"
+#include "gemm.hpp"
+#include "norm.hpp"
+
+using namespace phi;
+
+struct phi_model {
+  phi_config cfg;
+  std::vector<phi_layer_weights> layers;
+  const void* embed;
+  const void* final_norm;
+  phi_linear lm_head;
+  const float* rope_cos;  // [max_pos][head_dim / 2], in the caller's state buffer
+  const float* rope_sin;
+};
+
+namespace {
+
+constexpr int kMaxPos = 4096;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+phi_status launched() { return hipGetLastError() == hipSuccess ? PHI_OK : PHI_E_HIP; }
+
+// ---------------------------------------------------------------- workspace
+struct PrefillPlan {
+  int T, S, s_pad;
+  size_t off_x, off_xn, off_q, off_k, off_vt, off_attn, off_act, total;
+};
+
+PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
+  PrefillPlan p;
+  const size_t as = c.wtype == PHI_WT_F32 ? 4 : 2;
+  p.T = batch * seq;
+  p.S = seq;
+  p.s_pad = (int)round_up((size_t)seq, 64);
+  const size_t T = (size_t)p.T, H = (size_t)c.hidden, hd = (size_t)c.head_dim;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = round_up(o + bytes, 256); return r; };
+  p.off_x = take(T * H * 4);
+  p.off_xn = take(T * H * as);
+  p.off_q = take((size_t)batch * c.n_heads * seq * hd * as);
+  p.off_k = take((size_t)batch * c.n_kv_heads * seq * hd * as);
+  p.off_vt = take((size_t)batch * c.n_kv_heads * hd * p.s_pad * as);
+  p.off_attn = take(T * c.n_heads * hd * as);
+  p.off_act = take(T * (size_t)c.intermediate * as);
+  p.total = o;
+  return p;
+}
+
+bool check_config(const phi_config* c) {
+  return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && c->head_dim == 96 &&
+         c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
+         (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 64 && c->intermediate % 64 == 0 &&
+         c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 && c->max_pos <= kMaxPos;
+}
+
+// ---------------------------------------------------------------- GEMM dispatch
+template <int EPI>
+struct MfmaCfg { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2; };
+template <>
+struct MfmaCfg<EPI_QKV> { static constexpr int BM = 128, BN = 192, WGM = 2, WGN = 2; };
+
+template <int EPI>
+struct SimtCfg { static constexpr int BN = 64; };
+template <>
+struct SimtCfg<EPI_QKV> { static constexpr int BN = 96; };
+
+template <int EPI>
+phi_status gemm(int wtype, GemmArgs a, hipStream_t st) {
+  if (wtype == PHI_WT_F32) {
+    constexpr int BN = SimtCfg<EPI>::BN;
+    a.tiles_m = (a.M + 31) / 32;
+    a.tiles_n = EPI == EPI_SILU ? (a.N / 2) / (BN / 2) : (a.N + BN - 1) / BN;
+    const int tiles = a.tiles_m * a.tiles_n;
+    hipLaunchKernelGGL((phi_gemm_simt_f32_kernel<BN, EPI>), dim3(tiles), dim3(256), 0, st, a);
+    return launched();
+  }
+  using C = MfmaCfg<EPI>;
+  a.tiles_m = (a.M + C::BM - 1) / C::BM;
+  a.tiles_n = EPI == EPI_SILU ? (a.N / 2) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int grid = (tiles + 7) / 8 * 8;
+  constexpr int NT = C::WGM * C::WGN * 64;
+  if (wtype == PHI_WT_I8)
+    hipLaunchKernelGGL((phi_gemm_mfma_kernel<C::BM, C::BN, C::WGM, C::WGN, true, EPI>), dim3(grid), dim3(NT), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((phi_gemm_mfma_kernel<C::BM, C::BN, C::WGM, C::WGN, false, EPI>), dim3(grid), dim3(NT), 0,
+                       st, a);
+  return launched();
+}
+
+phi_status attention(bool f32, AttnArgs a, int batch, hipStream_t st) {
+  a.scale_log2 = kLog2e / sqrtf(96.0f);
+  if (f32) {
+    hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
+    return launched();
+  }
+  // more queries per workgroup when there are enough workgroups to fill the chip
+  const long units = (long)batch * a.nh;
+  if (units * ((a.S + 127) / 128) >= 512)
+    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<4>, dim3((a.S + 127) / 128, a.nh, batch), dim3(256), 0, st, a);
+  else if (units * ((a.S + 63) / 64) >= 256)
+    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<2>, dim3((a.S + 63) / 64, a.nh, batch), dim3(128), 0, st, a);
+  else
+    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<1>, dim3((a.S + 31) / 32, a.nh, batch), dim3(64), 0, st, a);
+  return launched();
+}
+
+template <class ET, class AT>
+phi_status norm(bool embed, NormArgs a, hipStream_t st) {
+  const dim3 grid((a.T + 3) / 4);
+  if (embed) hipLaunchKernelGGL((phi_norm_embed_kernel<ET, AT>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((phi_norm_rms_kernel<ET, AT>), grid, dim3(256), 0, st, a);
+  return launched();
+}
+
+template <class AT>
+phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, float* logits, char* ws,
+                   hipStream_t st) {
+  const phi_config& c = m->cfg;
+  const PrefillPlan p = plan_prefill(c, batch, seq);
+  const int T = p.T, H = c.hidden, I = c.intermediate, hd = c.head_dim;
+  float* x = reinterpret_cast<float*>(ws + p.off_x);
+  void* xn = ws + p.off_xn;
+  void* attn = ws + p.off_attn;
+  void* act = ws + p.off_act;
+  const int wt = c.wtype;
+
+  NormArgs na{};
+  na.ids = ids;
+  na.embed = m->embed;
+  na.x = x;
+  na.xn = xn;
+  na.T = T;
+  na.H = H;
+  na.V = c.vocab;
+  na.eps = c.rms_eps;
+  na.gain = m->layers[0].ln1;
+  phi_status s = norm<AT, AT>(true, na, st);
+  if (s) return s;
+
+  GemmArgs base{};
+  base.M = T;
+  base.S = seq;
+  base.s_pad = p.s_pad;
+  base.nh = c.n_heads;
+  base.nkv = c.n_kv_heads;
+  base.hd = hd;
+  base.rope_cos = m->rope_cos;
+  base.rope_sin = m->rope_sin;
+
+  AttnArgs aa{};
+  aa.q = ws + p.off_q;
+  aa.k = ws + p.off_k;
+  aa.vt = ws + p.off_vt;
+  aa.out = attn;
+  aa.S = seq;
+  aa.s_pad = p.s_pad;
+  aa.nh = c.n_heads;
+  aa.nkv = c.n_kv_heads;
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const phi_layer_weights& L = m->layers[l];
+    GemmArgs g = base;
+    g.A = xn;
+    g.W = L.qkv.w;
+    g.scale = L.qkv.scale;
+    g.N = (c.n_heads + 2 * c.n_kv_heads) * hd;
+    g.K = H;
+    g.q = const_cast<void*>(aa.q);
+    g.k = const_cast<void*>(aa.k);
+    g.vt = const_cast<void*>(aa.vt);
+    if ((s = gemm<EPI_QKV>(wt, g, st))) return s;
+
+    if ((s = attention(wt == PHI_WT_F32, aa, batch, st))) return s;
+
+    g = base;
+    g.A = attn;
+    g.W = L.o.w;
+    g.scale = L.o.scale;
+    g.N = H;
+    g.K = c.n_heads * hd;
+    g.x = x;
+    g.ldx = H;
+    if ((s = gemm<EPI_RESID>(wt, g, st))) return s;
+
+    na.gain = L.ln2;
+    if ((s = norm<AT, AT>(false, na, st))) return s;
+
+    g = base;
+    g.A = xn;
+    g.W = L.gate_up.w;
+    g.scale = L.gate_up.scale;
+    g.N = 2 * I;
+    g.K = H;
+    g.act = act;
+    g.ld_act = I;
+    if ((s = gemm<EPI_SILU>(wt, g, st))) return s;
+
+    g = base;
+    g.A = act;
+    g.W = L.down.w;
+    g.scale = L.down.scale;
+    g.N = H;
+    g.K = I;
+    g.x = x;
+    g.ldx = H;
+    if ((s = gemm<EPI_RESID>(wt, g, st))) return s;
+
+    na.gain = l + 1 < c.n_layers ? m->layers[l + 1].ln1 : m->final_norm;
+    if ((s = norm<AT, AT>(false, na, st))) return s;
+  }
+
+  GemmArgs g = base;
+  g.A = xn;
+  g.W = m->lm_head.w;
+  g.scale = m->lm_head.scale;
+  g.N = c.vocab;
+  g.K = H;
+  g.out = logits;
+  g.ldo = c.vocab;
+  return gemm<EPI_F32>(wt, g, st);
+}
+
+// ---------------------------------------------------------------- decode plan
+struct DecodePlan {
+  int n_split, pages_per_split;
+  size_t off_ml, total;
+};
+
+DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
+  DecodePlan p;
+  const int np = (max_ctx + 15) / 16;
+  const long units = (long)batch * n_kv_heads;
+  int want = (int)((2048 + units - 1) / units);  // about 8 workgroups per CU
+  const int max_split = (np + 3) / 4;            // at least 4 pages (one per wave) per split
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  p.pages_per_split = (np + want - 1) / want;
+  p.n_split = (np + p.pages_per_split - 1) / p.pages_per_split;
+  const size_t parts = (size_t)batch * n_q_heads * p.n_split;
+  p.off_ml = round_up(parts * 128 * 4, 256);
+  p.total = p.off_ml + round_up(parts * 2 * 4, 256);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* phi_strerror(int32_t s) {
+  switch (s) {
+    case PHI_OK: return "ok";
+    case PHI_E_NULL: return "null pointer argument";
+    case PHI_E_SHAPE: return "unsupported shape";
+    case PHI_E_DTYPE: return "unsupported weight type";
+    case PHI_E_RANGE: return "value out of range";
+    case PHI_E_WORKSPACE: return "workspace or state buffer too small";
+    case PHI_E_ALIGN: return "device pointer not 16-byte aligned";
+    case PHI_E_HIP: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t phi_state_bytes(const phi_config* cfg) {
+  if (!cfg || cfg->max_pos < 1 || cfg->head_dim < 2) return 0;
+  return 2 * (size_t)cfg->max_pos * (cfg->head_dim / 2) * sizeof(float);
+}
+
+phi_status phi_load_fused(const phi_config* cfg, const phi_weights* w, void* state, size_t state_bytes,
+                          void* stream, phi_model** out) {
+  if (!cfg || !w || !state || !out || !w->layers || !w->embed || !w->final_norm || !w->lm_head.w)
+    return PHI_E_NULL;
+  if (cfg->wtype != PHI_WT_F32 && cfg->wtype != PHI_WT_F16 && cfg->wtype != PHI_WT_I8) return PHI_E_DTYPE;
+  if (!check_config(cfg)) return PHI_E_SHAPE;
+  if (!(cfg->rms_eps > 0.f) || !(cfg->rope_theta > 0.f)) return PHI_E_RANGE;
+  if (state_bytes < phi_state_bytes(cfg)) return PHI_E_WORKSPACE;
+  const bool i8 = cfg->wtype == PHI_WT_I8;
+  auto lin_ok = [&](const phi_linear& l) { return l.w && (i8 ? l.scale != nullptr : l.scale == nullptr); };
+  if (!lin_ok(w->lm_head)) return PHI_E_NULL;
+  if (!aligned16(state) || !aligned16(w->embed) || !aligned16(w->final_norm) || !aligned16(w->lm_head.w) ||
+      !aligned16(w->lm_head.scale))
+    return PHI_E_ALIGN;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const phi_layer_weights& L = w->layers[l];
+    if (!L.ln1 || !L.ln2 || !lin_ok(L.qkv) || !lin_ok(L.o) || !lin_ok(L.gate_up) || !lin_ok(L.down))
+      return PHI_E_NULL;
+    const void* ps[] = {L.ln1, L.ln2, L.qkv.w, L.qkv.scale, L.o.w, L.o.scale,
+                        L.gate_up.w, L.gate_up.scale, L.down.w, L.down.scale};
+    for (const void* p : ps)
+      if (!aligned16(p)) return PHI_E_ALIGN;
+  }
+
+  phi_model* m = new (std::nothrow) phi_model;
+  if (!m) return PHI_E_HIP;
+  m->cfg = *cfg;
+  m->layers.assign(w->layers, w->layers + cfg->n_layers);
+  m->embed = w->embed;
+  m->final_norm = w->final_norm;
+  m->lm_head = w->lm_head;
+
+  // RoPE tables: angle(p, i) = p * theta^(-2 i / head_dim), in double, stored fp32.
+  const int half = cfg->head_dim / 2;
+  const size_t n = (size_t)cfg->max_pos * half;
+  std::vector<float> tab(2 * n);
+  for (int p = 0; p < cfg->max_pos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+      tab[(size_t)p * half + i] = (float)cos(ang);
+      tab[n + (size_t)p * half + i] = (float)sin(ang);
+    }
+  hipStream_t st = as_stream(stream);
+  if (hipMemcpyAsync(state, tab.data(), 2 * n * sizeof(float), hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    delete m;
+    return PHI_E_HIP;
+  }
+  m->rope_cos = reinterpret_cast<const float*>(state);
+  m->rope_sin = m->rope_cos + n;
+  *out = m;
+  return PHI_OK;
+}
+
+size_t phi_workspace_bytes(const phi_model* m, int32_t batch, int32_t seq) {
+  if (!m || batch < 1 || seq < 1) return 0;
+  return plan_prefill(m->cfg, batch, seq).total;
+}
+
+phi_status phi_prefill_logits(const phi_model* m, const int32_t* ids, int32_t batch, int32_t seq, float* logits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!m || !ids || !logits || !workspace) return PHI_E_NULL;
+  if (batch < 1 || seq < 1) return PHI_E_SHAPE;
+  if (seq > m->cfg.max_pos) return PHI_E_RANGE;
+  if ((long long)batch * seq > (1 << 24)) return PHI_E_SHAPE;
+  if (workspace_bytes < plan_prefill(m->cfg, batch, seq).total) return PHI_E_WORKSPACE;
+  if (!aligned16(ids) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
+  hipStream_t st = as_stream(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (m->cfg.wtype == PHI_WT_F32) return forward<float>(m, ids, batch, seq, logits, ws, st);
+  return forward<f16>(m, ids, batch, seq, logits, ws, st);
+}
+
+void phi_free(phi_model* m) { delete m; }
+
+phi_status phi_linear_f32out(int32_t wtype, const void* a, const void* w, const void* scale, float* y, int32_t M,
+                             int32_t N, int32_t K, void* stream) {
+  if (!a || !w || !y) return PHI_E_NULL;
+  if (wtype != PHI_WT_F32 && wtype != PHI_WT_F16 && wtype != PHI_WT_I8) return PHI_E_DTYPE;
+  if ((wtype == PHI_WT_I8) != (scale != nullptr)) return PHI_E_NULL;
+  if (M < 1 || N < 4 || K < 64 || K % 64 || N % 4) return PHI_E_SHAPE;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(scale)) return PHI_E_ALIGN;
+  GemmArgs g{};
+  g.A = a;
+  g.W = w;
+  g.scale = scale;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.out = y;
+  g.ldo = N;
+  return gemm<EPI_F32>(wtype, g, as_stream(stream));
+}
+
+phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const void* scale, void* act, int32_t M,
+                            int32_t I, int32_t K, void* stream) {
+  if (!a || !w || !act) return PHI_E_NULL;
+  if (wtype != PHI_WT_F32 && wtype != PHI_WT_F16 && wtype != PHI_WT_I8) return PHI_E_DTYPE;
+  if ((wtype == PHI_WT_I8) != (scale != nullptr)) return PHI_E_NULL;
+  if (M < 1 || I < 64 || K < 64 || K % 64 || I % 64) return PHI_E_SHAPE;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(act) || !aligned16(scale)) return PHI_E_ALIGN;
+  GemmArgs g{};
+  g.A = a;
+  g.W = w;
+  g.scale = scale;
+  g.M = M;
+  g.N = 2 * I;
+  g.K = K;
+  g.act = act;
+  g.ld_act = I;
+  return gemm<EPI_SILU>(wtype, g, as_stream(stream));
+}
+
+size_t phi_attention_vt_stride(int32_t seq) { return seq < 1 ? 0 : round_up((size_t)seq, 64); }
+
+phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, const void* vt, void* out,
+                                 int32_t batch, int32_t seq, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 void* stream) {
+  if (!q || !k || !vt || !out) return PHI_E_NULL;
+  if (batch < 1 || seq < 1 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || head_dim != 96)
+    return PHI_E_SHAPE;
+  if (seq > kMaxPos) return PHI_E_RANGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out)) return PHI_E_ALIGN;
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.vt = vt;
+  a.out = out;
+  a.S = seq;
+  a.s_pad = (int)round_up((size_t)seq, 64);
+  a.nh = n_heads;
+  a.nkv = n_kv_heads;
+  return attention(act_f32 != 0, a, batch, as_stream(stream));
+}
+
+size_t attn_decode_k16v8_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                         int32_t max_ctx) {
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim != 128 || max_ctx < 1) return 0;
+  return plan_decode(batch, n_q_heads, n_kv_heads, max_ctx).total;
+}
+
+phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
+                             const int32_t* block_table, const int32_t* ctx_lens, int32_t batch, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t n_pages,
+                             int32_t max_pages, int32_t max_ctx, float sm_scale, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!q || !k_pool || !v_pool || !v_scale || !block_table || !ctx_lens || !out || !workspace) return PHI_E_NULL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || head_dim != 128 ||
+      page_size != 16 || n_pages < 1 || max_pages < 1)
+    return PHI_E_SHAPE;
+  const int G = n_q_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PHI_E_SHAPE;
+  if (max_ctx < 1 || max_ctx > max_pages * page_size || !(sm_scale > 0.f)) return PHI_E_RANGE;
+  if ((long long)n_pages * n_kv_heads * 16 * 128 * 2 > (1ll << 40)) return PHI_E_SHAPE;
+  const DecodePlan p = plan_decode(batch, n_q_heads, n_kv_heads, max_ctx);
+  if (workspace_bytes < p.total) return PHI_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
+    return PHI_E_ALIGN;
+  DecodeArgs a{};
+  a.q = reinterpret_cast<const f16*>(q);
+  a.k_pool = reinterpret_cast<const f16*>(k_pool);
+  a.v_pool = reinterpret_cast<const uint8_t*>(v_pool);
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + p.off_ml);
+  a.out = reinterpret_cast<f16*>(out);
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.n_pages = n_pages;
+  a.max_pages = max_pages;
+  a.n_split = p.n_split;
+  a.pages_per_split = p.pages_per_split;
+  a.scale_log2 = sm_scale * kLog2e;
+  hipStream_t st = as_stream(stream);
+  const dim3 grid(p.n_split, n_kv_heads, batch);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(phi_decode_split_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(phi_decode_split_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(phi_decode_split_kernel<4>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(phi_decode_split_kernel<8>, grid, dim3(256), 0, st, a); break;
+  }
+  if (hipGetLastError() != hipSuccess) return PHI_E_HIP;
+  hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
+  return launched();
+}
+
+int64_t phi_kv_pool_slots(int64_t budget_bytes, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t k_bytes, int32_t v_bytes, int32_t page_size) {
+  if (budget_bytes <= 0 || n_layers <= 0 || n_kv_heads <= 0 || head_dim <= 0 || k_bytes <= 0 || v_bytes <= 0 ||
+      page_size <= 0)
+    return -1;
+  const int64_t per_token = (int64_t)n_kv_heads * head_dim * (k_bytes + v_bytes);
+  const int64_t slots = budget_bytes / n_layers / per_token;
+  return slots / page_size * page_size;
+}
+
+}  // extern "C"

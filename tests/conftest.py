@@ -25,3 +25,31 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+# ---------------------------------------------------------------- GPU fixtures
+@pytest.fixture(scope="session")
+def phi():
+    import logits_parity_amd as phi_mod
+    phi_mod.lib()  # raises when libphi.so is missing: no fallback path
+    return phi_mod
+
+
+@pytest.fixture(scope="session")
+def mini_f16():
+    """Host float16 weights of the Phi-3-mini-shaped model (seed 1) and their
+    device copies."""
+    import synth
+    from logits_parity_amd.weights import to_device
+    ws = synth.WeightSet(synth.MINI)
+    dev = to_device(ws, synth.MINI.n_layers, "cuda")
+    return ws, dev
+
+
+@pytest.fixture(scope="session")
+def mini_w8():
+    import synth
+    from logits_parity_amd.weights import to_device
+    ws = synth.WeightSet(synth.MINI_W8)
+    dev = to_device(ws, synth.MINI_W8.n_layers, "cuda")
+    return ws, dev

@@ -1,0 +1,99 @@
+"""K16/V8 paged decode attention vs the fp64 oracle (GPU).
+
+Gate: for every (sequence, query head), ||o - o_ref|| / ||o_ref|| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu(phi, d, max_ctx=None, sm_scale=None):
+    D = d.q.shape[-1]
+    sm = 1 / np.sqrt(D) if sm_scale is None else sm_scale
+    mc = int(d.ctx_lens.max()) if max_ctx is None else max_ctx
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = phi.attn_decode_k16v8(t(d.q), t(d.k_pool), t(d.v_pool), t(d.v_scale), t(d.block_table),
+                                t(d.ctx_lens), mc, sm)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _ref(d, sm_scale=None):
+    D = d.q.shape[-1]
+    sm = 1 / np.sqrt(D) if sm_scale is None else sm_scale
+    return decode.decode_attention(d.q, d.k_pool, d.v_pool, d.v_scale, d.block_table, d.ctx_lens, sm)
+
+
+def _rel(got, ref):
+    return np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+
+
+@pytest.mark.parametrize("name", ["decode_k16v8_32x1024", "decode_k16v8_16x8192"])
+def test_decode_full_shapes(phi, name):
+    wl = synth.DECODE_WORKLOADS[name]
+    _say(name)
+    d = synth.decode_inputs(wl)
+    got = _gpu(phi, d)
+    ref = _ref(d)
+    rel = _rel(got, ref)
+    _say(f"  max rel L2 = {rel.max():.2e}")
+    assert rel.max() <= 2e-3
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_ragged_contexts(phi, G):
+    wl = synth.DecodeWorkload("t", batch=6, ctx=300, n_q_heads=2 * G, n_kv_heads=2)
+    lens = [1, 15, 16, 17, 255, 300]
+    _say(f"decode ragged G={G}")
+    d = synth.decode_inputs(wl, ctx_lens=lens)
+    got = _gpu(phi, d)
+    rel = _rel(got, _ref(d))
+    assert rel.max() <= 2e-3, rel.max()
+
+
+def test_decode_page_permutation_is_invisible(phi):
+    wl = synth.DecodeWorkload("t", batch=4, ctx=500, n_q_heads=8, n_kv_heads=2)
+    d = synth.decode_inputs(wl)
+    a = _gpu(phi, d)
+    perm = synth.permutation(99, "repage", wl.n_pages)
+    inv = np.argsort(perm)
+    d.k_pool, d.v_pool = d.k_pool[perm].copy(), d.v_pool[perm].copy()
+    d.block_table = inv[d.block_table].astype(np.int32)
+    b = _gpu(phi, d)
+    assert np.array_equal(a, b)
+
+
+def test_decode_unit_values_sum_to_one(phi):
+    wl = synth.DecodeWorkload("t", batch=3, ctx=200, n_q_heads=8, n_kv_heads=2)
+    d = synth.decode_inputs(wl)
+    d.v_pool[:] = 0x38
+    d.v_scale[:] = 1.0
+    got = _gpu(phi, d)
+    assert np.abs(got - 1).max() <= 1e-3
+
+
+def test_decode_bad_inputs_make_only_that_sequence_nan(phi):
+    wl = synth.DecodeWorkload("t", batch=3, ctx=64, n_q_heads=8, n_kv_heads=2)
+    d = synth.decode_inputs(wl)
+    d.block_table[1, 2] = wl.n_pages + 7
+    d.ctx_lens[2] = 0
+    got = _gpu(phi, d, max_ctx=64)
+    assert np.all(np.isfinite(got[0]))
+    assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
+    ref = _ref(d.__class__(d.wl, d.q[:1], d.k_pool, d.v_pool, d.v_scale, d.block_table[:1], d.ctx_lens[:1]))
+    assert _rel(got[:1], ref).max() <= 2e-3
+
+
+def test_decode_deterministic(phi):
+    wl = synth.DECODE_WORKLOADS["decode_k16v8_32x1024"]
+    d = synth.decode_inputs(wl)
+    assert np.array_equal(_gpu(phi, d), _gpu(phi, d))

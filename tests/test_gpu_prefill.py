@@ -1,0 +1,178 @@
+"""End-to-end prefill parity: ids -> logits through the C ABI vs the oracle (GPU).
+
+Gates: per-position logit cosine >= 0.99999 against the fp64 oracle and
+argmax agreement wherever the oracle's top-2 gap exceeds 1e-3 (absolute
+logits).  The int8 path is gated against the oracle run on the int8 weights
+(code * scale); its cosine against the float16 oracle is reported.
+
+Small cases run the oracle live.  Full Phi-3-mini shapes compare with oracle
+results stored under tests/golden/ (written by make_goldens.py, which calls
+only the oracle): full rows at sampled positions plus argmax and top-2 gap at
+every position.  The input digests stored with them must match.
+"""
+import hashlib
+import os
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import parity, prefill
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+COS_GATE = 0.99999
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(phi, cfg, dev_weights, ids):
+    m = phi.phi_load_fused(cfg, dev_weights)
+    out = m.prefill_logits(torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _gate(got, ref):
+    s = parity.summary(got.reshape(-1, got.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    _say(f"  min_cos={s['min_cos']:.9f} gated={s['gated']} agree={s['gated_agree']}")
+    assert np.all(np.isfinite(got))
+    assert s["min_cos"] >= COS_GATE, s
+    assert not s["failures"], s
+    return s
+
+
+@pytest.mark.parametrize("batch,seq", [(1, 16), (2, 13), (3, 1)])
+def test_tiny_f32_vs_oracle(phi, batch, seq):
+    from logits_parity_amd.weights import to_device
+    cfg = synth.TINY
+    _say(f"tiny f32 {batch}x{seq}")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, batch, seq)
+    got = _run(phi, cfg, to_device(ws, cfg.n_layers), ids)
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    s = _gate(got, ref)
+    assert s["min_cos"] > 1 - 1e-9
+
+
+@pytest.mark.parametrize("wtype", ["f16", "i8"])
+def test_tiny_low_precision_vs_oracle(phi, wtype):
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.TINY, wtype=wtype)
+    _say(f"tiny {wtype}")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 2, 40)
+    got = _run(phi, cfg, to_device(ws, cfg.n_layers), ids)
+    _gate(got, prefill.prefill_logits(cfg, ws, ids))
+
+
+def test_tiny_f32_gqa_unit_gains(phi):
+    # harder regime: unit norm gains, GQA grouping
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.TINY, n_kv_heads=2, norm_gain="ones")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 1, 33)
+    got = _run(phi, cfg, to_device(ws, cfg.n_layers), ids)
+    _gate(got, prefill.prefill_logits(cfg, ws, ids))
+
+
+def test_tiny_bad_id_gives_nan_rows_only_in_its_sequence(phi):
+    from logits_parity_amd.weights import to_device
+    cfg = synth.TINY
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 2, 8).copy()
+    ids[1, 3] = cfg.vocab + 5
+    got = _run(phi, cfg, to_device(ws, cfg.n_layers), ids)
+    assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1, :3]))
+    assert np.all(np.isnan(got[1, 3:]))
+
+
+def test_tiny_errors_are_reported(phi):
+    from logits_parity_amd.weights import to_device
+    cfg = synth.TINY
+    dev = to_device(synth.WeightSet(cfg), cfg.n_layers)
+    m = phi.phi_load_fused(cfg, dev)
+    ids = torch.zeros((1, cfg.max_pos + 1), dtype=torch.int32, device="cuda")
+    with pytest.raises(phi.PhiError) as e:
+        m.prefill_logits(ids)
+    assert e.value.status == 4  # PHI_E_RANGE
+    ids = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(phi.PhiError) as e:
+        m.prefill_logits(ids, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 5  # PHI_E_WORKSPACE
+
+
+# ---------------------------------------------------------------- full shapes
+def _golden(name):
+    path = os.path.join(GOLDEN, name + ".npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return np.load(path)
+
+
+def _check_golden(g, got_flat, ids, digest, prefix=""):
+    """Oracle-trust first: the stored results must belong to these exact inputs."""
+    assert str(g["ids_sha256"]) == hashlib.sha256(np.ascontiguousarray(ids, np.int32).tobytes()).hexdigest()
+    assert str(g[prefix + "weights_sha256"]) == digest
+    pos = g["pos"]
+    rows = g[prefix + "rows"].astype(np.float64)
+    cos = parity.row_cosines(got_flat[pos], rows)
+    gap = g[prefix + "gap"]
+    agree = np.argmax(got_flat, axis=1) == g[prefix + "argmax"]
+    gated = gap > 1e-3
+    fails = np.nonzero(gated & ~agree)[0]
+    _say(f"  sampled min_cos={cos.min():.9f} mean={cos.mean():.9f}; argmax gated={gated.sum()} "
+         f"agree={(agree & gated).sum()} all-agree={agree.sum()}/{len(agree)}")
+    return cos, fails
+
+
+@pytest.fixture(scope="module")
+def mini_digest(mini_f16):
+    return mini_f16[0].digest()
+
+
+@pytest.mark.parametrize("name", ["mini_f16_1x512", "mini_f16_1x4096"])
+def test_mini_f16_vs_stored_oracle(phi, mini_f16, mini_digest, name):
+    wl = synth.PREFILL_WORKLOADS[name]
+    _say(f"{name}")
+    g = _golden(name)
+    ids = synth.token_ids(wl.cfg, wl.batch, wl.seq)
+    got = _run(phi, wl.cfg, mini_f16[1], ids).reshape(-1, wl.cfg.vocab).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    cos, fails = _check_golden(g, got, ids, mini_digest)
+    assert cos.min() >= COS_GATE
+    assert len(fails) == 0, fails[:20]
+
+
+def test_mini_w8_vs_stored_oracle(phi, mini_w8, mini_digest):
+    name = "mini_w8_4x1024"
+    wl = synth.PREFILL_WORKLOADS[name]
+    _say(name)
+    g = _golden(name)
+    ids = synth.token_ids(wl.cfg, wl.batch, wl.seq)
+    got = _run(phi, wl.cfg, mini_w8[1], ids).reshape(-1, wl.cfg.vocab).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    cos, fails = _check_golden(g, got, ids, mini_w8[0].digest())
+    assert cos.min() >= COS_GATE
+    assert len(fails) == 0, fails[:20]
+    # reported: distance to the float16 oracle is the quantisation's, not the kernel's
+    cos16, _ = _check_golden(g, got, ids, mini_digest, prefix="f16_")
+    ref_i8 = g["rows"].astype(np.float64)
+    floor = parity.row_cosines(ref_i8, g["f16_rows"].astype(np.float64))
+    _say(f"  vs f16 oracle: min_cos={cos16.min():.7f}; oracle(int8) vs oracle(f16) floor={floor.min():.7f}")
+    assert abs(cos16.min() - floor.min()) < 1e-5
+
+
+def test_mini_prefix_invariance_and_determinism(phi, mini_f16):
+    wl = synth.PREFILL_WORKLOADS["mini_f16_1x512"]
+    ids = synth.token_ids(wl.cfg, 1, 512)
+    a = _run(phi, wl.cfg, mini_f16[1], ids)
+    b = _run(phi, wl.cfg, mini_f16[1], ids)
+    assert np.array_equal(a, b)
+    c = _run(phi, wl.cfg, mini_f16[1], ids[:, :200])
+    cos = parity.row_cosines(c[0], a[0, :200])
+    assert cos.min() > 1 - 1e-9
