@@ -68,7 +68,7 @@ typedef struct phi_config {
   int32_t n_heads;      /* query heads                                        */
   int32_t n_kv_heads;   /* divides n_heads (n_kv_heads == n_heads: MHA)       */
   int32_t head_dim;     /* 96 ([P1] section 2)                                */
-  int32_t intermediate; /* I; multiple of 64                                  */
+  int32_t intermediate; /* I; multiple of 128                                 */
   int32_t vocab;        /* V; multiple of 4                                   */
   int32_t max_pos;      /* longest sequence; at most 4096 ([P1] section 4)   */
   float rms_eps;
@@ -152,7 +152,7 @@ phi_status phi_linear_f32out(int32_t wtype, const void* a, const void* w, const 
  * its SiLU(gate) * up epilogue, where w = [w_gate; w_up] is the single fused
  * tensor of 2 I rows, gate rows first ([P1] section 1).  Same kernel as the
  * prefill's MLP step.  Types as in phi_linear_f32out; act is float32 for
- * PHI_WT_F32 and binary16 otherwise.  I and K must be multiples of 64. */
+ * PHI_WT_F32 and binary16 otherwise.  I must be a multiple of 128 and K of 64. */
 phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const void* scale, void* act,
                             int32_t M, int32_t I, int32_t K, void* stream);
 

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -37,10 +38,84 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 phi_status launched() { return hipGetLastError() == hipSuccess ? PHI_OK : PHI_E_HIP; }
 
+// ---------------------------------------------------------------- GEMM plans
+using CfgL = TileCfg<256, 256, 2, 2>;   // wave tile 128 x 128
+using CfgM = TileCfg<256, 128, 2, 2>;   // wave tile 128 x 64
+using CfgS = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64
+using CfgQL = TileCfg<256, 192, 2, 2>;  // wave tile 128 x 96 (one head per wave)
+using CfgQS = TileCfg<128, 192, 2, 2>;  // wave tile 64 x 96
+enum CfgId { C_L, C_M, C_S, C_QL, C_QS };
+
+struct GemmPlan {
+  int cfg, tiles_m, tiles_n, splits, kpt;
+};
+
+constexpr int kCUs = 256;
+
+inline void cfg_dims(int cfg, int& bm, int& bn) {
+  switch (cfg) {
+    case C_L: bm = 256; bn = 256; break;
+    case C_M: bm = 256; bn = 128; break;
+    case C_S: bm = 128; bn = 128; break;
+    case C_QL: bm = 256; bn = 192; break;
+    default: bm = 128; bn = 192; break;
+  }
+}
+
+// Tile shape per GEMM role and token count: large wave tiles keep LDS traffic
+// per MFMA low; at small M the residual GEMMs (N = hidden) have too few tiles
+// for 256 CUs, so K is split until every CU has work.
+// int8 weights stage through VGPRs, which the 256 x 256 tile cannot afford
+// next to its 256 accumulators, so they take the 256 x 128 tile instead.
+GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8) {
+  GemmPlan p{};
+  if (epi == EPI_QKV) p.cfg = M >= 1024 ? C_QL : C_QS;
+  else if (epi == EPI_SILU) p.cfg = (M >= 1024 && !w8) ? C_L : C_M;
+  else if (epi == EPI_F32) p.cfg = w8 ? C_M : C_L;
+  else p.cfg = M >= 2048 ? C_M : C_S;
+  int bm, bn;
+  cfg_dims(p.cfg, bm, bn);
+  p.tiles_m = (M + bm - 1) / bm;
+  p.tiles_n = epi == EPI_SILU ? (N / 2) / (bn / 2) : (N + bn - 1) / bn;
+  const int nk = K / 64;
+  int s = 1;
+  if (epi == EPI_RESID)
+    while (p.tiles_m * p.tiles_n * s < kCUs && nk / (2 * s) >= 4) s *= 2;
+  p.kpt = (nk + s - 1) / s;
+  p.splits = (nk + p.kpt - 1) / p.kpt;
+  return p;
+}
+
+template <class C, bool W8, int EPI>
+void launch_mfma(GemmArgs a, hipStream_t st) {
+  const int units = a.tiles_m * a.tiles_n * a.splits;
+  const int grid = (units + 7) / 8 * 8;
+  hipLaunchKernelGGL((phi_gemm_mfma_kernel<C, W8, EPI>), dim3(grid), dim3(C::NT), 0, st, a);
+}
+
+template <bool W8, int EPI>
+void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
+  if constexpr (EPI == EPI_QKV) {
+    if (cfg == C_QL) launch_mfma<CfgQL, W8, EPI>(a, st);
+    else launch_mfma<CfgQS, W8, EPI>(a, st);
+  } else if constexpr (EPI == EPI_SILU) {
+    if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
+    else if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st);
+    else launch_mfma<CfgM, W8, EPI>(a, st);
+  } else if constexpr (EPI == EPI_F32) {
+    if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
+    else launch_mfma<CfgL, W8, EPI>(a, st);
+  } else {
+    if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st);
+    else launch_mfma<CfgS, W8, EPI>(a, st);
+  }
+}
+
 // ---------------------------------------------------------------- workspace
 struct PrefillPlan {
   int T, S, s_pad;
-  size_t off_x, off_xn, off_q, off_k, off_vt, off_attn, off_act, total;
+  GemmPlan qkv, o, gu, down, lm;
+  size_t off_x, off_xn, off_q, off_k, off_vt, off_attn, off_act, off_part, total;
 };
 
 PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
@@ -49,7 +124,14 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.T = batch * seq;
   p.S = seq;
   p.s_pad = (int)round_up((size_t)seq, 64);
-  const size_t T = (size_t)p.T, H = (size_t)c.hidden, hd = (size_t)c.head_dim;
+  const int H = c.hidden, hd = c.head_dim, I = c.intermediate;
+  const bool w8 = c.wtype == PHI_WT_I8;
+  p.qkv = plan_gemm(EPI_QKV, p.T, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8);
+  p.o = plan_gemm(EPI_RESID, p.T, H, c.n_heads * hd, w8);
+  p.gu = plan_gemm(EPI_SILU, p.T, 2 * I, H, w8);
+  p.down = plan_gemm(EPI_RESID, p.T, H, I, w8);
+  p.lm = plan_gemm(EPI_F32, p.T, c.vocab, H, w8);
+  const size_t T = (size_t)p.T;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = round_up(o + bytes, 256); return r; };
   p.off_x = take(T * H * 4);
@@ -58,7 +140,9 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.off_k = take((size_t)batch * c.n_kv_heads * seq * hd * as);
   p.off_vt = take((size_t)batch * c.n_kv_heads * hd * p.s_pad * as);
   p.off_attn = take(T * c.n_heads * hd * as);
-  p.off_act = take(T * (size_t)c.intermediate * as);
+  p.off_act = take(T * (size_t)I * as);
+  const int max_split = c.wtype == PHI_WT_F32 ? 0 : std::max(p.o.splits, p.down.splits);
+  p.off_part = take(max_split > 1 ? (size_t)max_split * T * H * 4 : 0);
   p.total = o;
   return p;
 }
@@ -66,43 +150,45 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
 bool check_config(const phi_config* c) {
   return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && c->head_dim == 96 &&
          c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
-         (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 64 && c->intermediate % 64 == 0 &&
+         (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 128 && c->intermediate % 128 == 0 &&
          c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 && c->max_pos <= kMaxPos;
 }
 
 // ---------------------------------------------------------------- GEMM dispatch
 template <int EPI>
-struct MfmaCfg { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2; };
-template <>
-struct MfmaCfg<EPI_QKV> { static constexpr int BM = 128, BN = 192, WGM = 2, WGN = 2; };
-
-template <int EPI>
 struct SimtCfg { static constexpr int BN = 64; };
 template <>
 struct SimtCfg<EPI_QKV> { static constexpr int BN = 96; };
 
+// Runs one GEMM; returns the number of K splits whose partials the caller
+// must reduce (0 when the epilogue completed the result).
 template <int EPI>
-phi_status gemm(int wtype, GemmArgs a, hipStream_t st) {
+phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* partials = nullptr) {
+  if (partials) *partials = 0;
   if (wtype == PHI_WT_F32) {
     constexpr int BN = SimtCfg<EPI>::BN;
     a.tiles_m = (a.M + 31) / 32;
     a.tiles_n = EPI == EPI_SILU ? (a.N / 2) / (BN / 2) : (a.N + BN - 1) / BN;
+    a.splits = 1;
     const int tiles = a.tiles_m * a.tiles_n;
     hipLaunchKernelGGL((phi_gemm_simt_f32_kernel<BN, EPI>), dim3(tiles), dim3(256), 0, st, a);
     return launched();
   }
-  using C = MfmaCfg<EPI>;
-  a.tiles_m = (a.M + C::BM - 1) / C::BM;
-  a.tiles_n = EPI == EPI_SILU ? (a.N / 2) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
-  const int tiles = a.tiles_m * a.tiles_n;
-  const int grid = (tiles + 7) / 8 * 8;
-  constexpr int NT = C::WGM * C::WGN * 64;
-  if (wtype == PHI_WT_I8)
-    hipLaunchKernelGGL((phi_gemm_mfma_kernel<C::BM, C::BN, C::WGM, C::WGN, true, EPI>), dim3(grid), dim3(NT), 0,
-                       st, a);
-  else
-    hipLaunchKernelGGL((phi_gemm_mfma_kernel<C::BM, C::BN, C::WGM, C::WGN, false, EPI>), dim3(grid), dim3(NT), 0,
-                       st, a);
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.splits = p.splits;
+  a.kt_per_split = p.kpt;
+  const bool w8 = wtype == PHI_WT_I8;
+  if constexpr (EPI == EPI_RESID) {
+    if (p.splits > 1) {
+      if (partials) *partials = p.splits;
+      if (w8) launch_cfg<true, EPI_PARTIAL>(p.cfg, a, st);
+      else launch_cfg<false, EPI_PARTIAL>(p.cfg, a, st);
+      return launched();
+    }
+  }
+  if (w8) launch_cfg<true, EPI>(p.cfg, a, st);
+  else launch_cfg<false, EPI>(p.cfg, a, st);
   return launched();
 }
 
@@ -141,6 +227,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   void* xn = ws + p.off_xn;
   void* attn = ws + p.off_attn;
   void* act = ws + p.off_act;
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
   const int wt = c.wtype;
 
   NormArgs na{};
@@ -148,6 +235,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   na.embed = m->embed;
   na.x = x;
   na.xn = xn;
+  na.part = part;
   na.T = T;
   na.H = H;
   na.V = c.vocab;
@@ -187,7 +275,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.q = const_cast<void*>(aa.q);
     g.k = const_cast<void*>(aa.k);
     g.vt = const_cast<void*>(aa.vt);
-    if ((s = gemm<EPI_QKV>(wt, g, st))) return s;
+    if ((s = gemm<EPI_QKV>(wt, g, p.qkv, st))) return s;
 
     if ((s = attention(wt == PHI_WT_F32, aa, batch, st))) return s;
 
@@ -199,7 +287,8 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.K = c.n_heads * hd;
     g.x = x;
     g.ldx = H;
-    if ((s = gemm<EPI_RESID>(wt, g, st))) return s;
+    g.out = part;
+    if ((s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit))) return s;
 
     na.gain = L.ln2;
     if ((s = norm<AT, AT>(false, na, st))) return s;
@@ -212,7 +301,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.K = H;
     g.act = act;
     g.ld_act = I;
-    if ((s = gemm<EPI_SILU>(wt, g, st))) return s;
+    if ((s = gemm<EPI_SILU>(wt, g, p.gu, st))) return s;
 
     g = base;
     g.A = act;
@@ -222,7 +311,8 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.K = I;
     g.x = x;
     g.ldx = H;
-    if ((s = gemm<EPI_RESID>(wt, g, st))) return s;
+    g.out = part;
+    if ((s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit))) return s;
 
     na.gain = l + 1 < c.n_layers ? m->layers[l + 1].ln1 : m->final_norm;
     if ((s = norm<AT, AT>(false, na, st))) return s;
@@ -236,7 +326,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   g.K = H;
   g.out = logits;
   g.ldo = c.vocab;
-  return gemm<EPI_F32>(wt, g, st);
+  return gemm<EPI_F32>(wt, g, p.lm, st);
 }
 
 // ---------------------------------------------------------------- decode plan
@@ -375,7 +465,7 @@ phi_status phi_linear_f32out(int32_t wtype, const void* a, const void* w, const 
   g.K = K;
   g.out = y;
   g.ldo = N;
-  return gemm<EPI_F32>(wtype, g, as_stream(stream));
+  return gemm<EPI_F32>(wtype, g, plan_gemm(EPI_F32, M, N, K, wtype == PHI_WT_I8), as_stream(stream));
 }
 
 phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const void* scale, void* act, int32_t M,
@@ -383,7 +473,7 @@ phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const v
   if (!a || !w || !act) return PHI_E_NULL;
   if (wtype != PHI_WT_F32 && wtype != PHI_WT_F16 && wtype != PHI_WT_I8) return PHI_E_DTYPE;
   if ((wtype == PHI_WT_I8) != (scale != nullptr)) return PHI_E_NULL;
-  if (M < 1 || I < 64 || K < 64 || K % 64 || I % 64) return PHI_E_SHAPE;
+  if (M < 1 || I < 128 || K < 64 || K % 64 || I % 128) return PHI_E_SHAPE;
   if (!aligned16(a) || !aligned16(w) || !aligned16(act) || !aligned16(scale)) return PHI_E_ALIGN;
   GemmArgs g{};
   g.A = a;
@@ -394,7 +484,7 @@ phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const v
   g.K = K;
   g.act = act;
   g.ld_act = I;
-  return gemm<EPI_SILU>(wtype, g, as_stream(stream));
+  return gemm<EPI_SILU>(wtype, g, plan_gemm(EPI_SILU, M, 2 * I, K, wtype == PHI_WT_I8), as_stream(stream));
 }
 
 size_t phi_attention_vt_stride(int32_t seq) { return seq < 1 ? 0 : round_up((size_t)seq, 64); }

@@ -1,39 +1,55 @@
 // Prefill GEMMs: y[M][N] = a[M][K] w[N][K]^T with fused epilogues.
 //
-// Two cores share one set of epilogues:
-//  - phi_gemm_mfma_kernel: binary16 activations, binary16 or int8 weights,
-//    v_mfma_f32_32x32x16_f16 on 64-wide waves, fp32 accumulation.  Tiles are
-//    staged through LDS in 16-byte chunks with an XOR swizzle (chunk c of row
-//    r sits at c ^ (r & 7)) so each MFMA operand read is one conflict-free
-//    ds_read_b128.  The K loop double-buffers LDS and overlaps the next tile's
-//    global loads with the current tile's MFMAs.  int8 weights are widened to
-//    binary16 exactly (|q| <= 127) on their way into LDS; the per-row scale
-//    multiplies the fp32 accumulator, since it factors out of the K sum.
-//  - phi_gemm_simt_f32_kernel: fp32 FMA core for the float32 model.
-// After the K loop the accumulator tile is written to LDS (fp32) and the
-// epilogue reads it row-wise, so every global store is a 16-byte vector:
-//  EPI_F32    logits: out[m][n] = acc
-//  EPI_RESID  residual: x[m][n] += acc
-//  EPI_SILU   fused gate/up: the tile's first half holds gate rows, the second
-//             half the matching up rows; act[m][n] = silu(gate) * up
-//  EPI_QKV    fused Q/K/V: tiles cover whole heads; RoPE rotates pairs
-//             (d, d + hd/2) of Q and K heads by angle pos * theta^(-2d/hd)
-//             (tables precomputed); Q, K go to [B][heads][S][hd], V to
-//             V^T [B][kv_heads][hd][s_pad].
+// MFMA core (binary16 activations; binary16 or int8 weights):
+//  - 4 waves of 64 lanes, each owning a WM x WN sub-tile built from
+//    v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators.
+//  - K is walked in steps of 64 through two LDS stages.  binary16 operands go
+//    global -> LDS directly (global_load_lds_dwordx4, no VGPR staging): one
+//    wave instruction fills 1 KB = 8 rows of 128 B.  int8 weights are loaded
+//    into VGPRs, widened exactly to binary16 (|q| <= 127) and written to LDS;
+//    their per-row scale multiplies the fp32 accumulator (it factors out of
+//    the K sum).
+//  - Rows are stored with an XOR swizzle of their 16-byte chunks,
+//    chunk' = chunk ^ ((row >> 1) & 7): 16 lanes reading 16 consecutive rows
+//    at one logical chunk touch 16 distinct 16-byte bank groups of the
+//    256-byte LDS bank row, so fragment reads are conflict free.
+//  - Each k-step's fragment reads for step s+1 are issued before the MFMAs of
+//    step s (scheduling barriers keep the compiler from re-serialising them).
+//  - Split-K: a launch may cut K into `splits` ranges; each writes an fp32
+//    partial tile that the next kernel (the residual + RMSNorm) reduces in a
+//    fixed order, so results do not depend on scheduling.
+//  - Workgroups map to tiles so that consecutive tiles of one weight column
+//    block run on the same XCD (workgroups go round-robin over the 8 XCDs),
+//    sharing that XCD's L2 for the weight tile.
+// Epilogues work on the accumulator registers (lane l of a 32x32 block holds
+// column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4, v < 16):
+//  EPI_F32      logits: out[m][n] = acc
+//  EPI_RESID    residual: x[m][n] += acc
+//  EPI_PARTIAL  split-K: part[split][m][n] = acc
+//  EPI_SILU     fused gate/up: the tile reads weight rows in 32-row blocks
+//               alternating gate, up for the same outputs, so a lane holds
+//               gate and up of one output: act = silu(gate) * up
+//  EPI_QKV      fused Q/K/V, one 96-wide head per wave: the head's weight rows
+//               are read in the order d = 0..31 | 48..79 | 32..47, 80..95 so
+//               that RoPE pairs (d, d + 48) sit in one lane (first two blocks)
+//               or in lanes l and l ^ 16 (third block).  RoPE runs on the fp32
+//               accumulator; Q, K go to [B][heads][S][96], V to
+//               V^T [B][kv_heads][96][s_pad].
+// fp32 core (float32 model): a SIMT kernel with an LDS-staged epilogue.
 #pragma once
 #include "common.hpp"
 
 namespace phi {
 
-enum { EPI_F32 = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3 };
+enum { EPI_F32 = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3, EPI_PARTIAL = 4 };
 
 struct GemmArgs {
   const void* A;      // [M][K] activations
   const void* W;      // [N][K] weights (f16, int8 or f32)
   const void* scale;  // binary16 [N] (int8 weights)
   int M, N, K;        // N = rows of W (2 I for the fused gate/up)
-  int tiles_m, tiles_n;
-  float* out;         // EPI_F32: [M][ldo]
+  int tiles_m, tiles_n, splits, kt_per_split;
+  float* out;         // EPI_F32: [M][ldo]; EPI_PARTIAL: [splits][M][N]
   int ldo;
   float* x;           // EPI_RESID: [M][ldx]
   int ldx;
@@ -47,35 +63,295 @@ struct GemmArgs {
   int S, s_pad, nh, nkv, hd;
 };
 
-// Row of W that local row r of N-tile tn reads.
+// ---------------------------------------------------------------- row maps
+// Weight row read by tile-local row r of N-tile tn (MFMA core).
 template <int EPI, int BN>
-__device__ __forceinline__ int w_row(const GemmArgs& a, int tn, int r) {
+__device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
   if constexpr (EPI == EPI_SILU) {
-    constexpr int H2 = BN / 2;
-    const int I = a.N >> 1;
-    return r < H2 ? tn * H2 + r : I + tn * H2 + (r - H2);
+    // 32-row blocks alternate gate / up; block pair p covers outputs tn*BN/2 + 32p ..
+    const int blk = r >> 5, p = blk >> 1;
+    const int out = tn * (BN / 2) + p * 32 + (r & 31);
+    return (blk & 1) ? (a.N >> 1) + out : out;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int head_base = tn * BN + (r / 96) * 96;
+    const int j = r % 96;
+    const int d = j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
+    const int n = head_base + d;
+    return n < a.N ? n : a.N - 1;
   } else {
     const int n = tn * BN + r;
     return n < a.N ? n : a.N - 1;
   }
 }
 
+// ---------------------------------------------------------------- MFMA core
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+// s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
+#define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  f16x8 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = (f16)(float)(int8_t)(lo >> (8 * e));
+    o[4 + e] = (f16)(float)(int8_t)(hi >> (8 * e));
+  }
+  return o;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NT = WGM * WGN * 64, NW = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+};
+
+template <class C, bool W8, int EPI>
+__global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
+  constexpr int NT = C::NT, NW = C::NW, BK = 64;
+  constexpr int STAGE = (BM + BN) * BK;              // f16 elements per LDS stage
+  constexpr int INS_A = BM * 8 / 64;                 // 1 KB DMA instructions for A per stage
+  constexpr int INS_W = W8 ? 0 : BN * 8 / 64;
+  constexpr int LPW = (INS_A + INS_W) / NW;          // DMA instructions per wave per stage
+  constexpr int CB8 = W8 ? BN * 4 / NT : 0;          // int8 16-byte chunks per thread per stage
+  static_assert(LPW * NW == INS_A + INS_W, "stage split");
+  static_assert(!W8 || CB8 * NT == BN * 4, "int8 split");
+  static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
+  static_assert(EPI != EPI_QKV || WN == 96, "QKV: one head per wave");
+  static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
+
+  __shared__ __attribute__((aligned(1024))) f16 smem[2 * STAGE];
+
+  const int n_units = a.tiles_m * a.tiles_n * a.splits;
+  const int unit = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (unit >= n_units) return;
+  const int tm = unit % a.tiles_m;
+  const int tn = (unit / a.tiles_m) % a.tiles_n;
+  const int split = unit / (a.tiles_m * a.tiles_n);
+  const int m0 = tm * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int K = a.K;
+  const f16* A = reinterpret_cast<const f16*>(a.A);
+
+  // DMA sources: instruction j = wave + NW * t fills LDS slots [64 j, 64 j + 64)
+  int src_off[LPW > 0 ? LPW : 1];
+  bool src_is_w[LPW > 0 ? LPW : 1];
+#pragma unroll
+  for (int t = 0; t < LPW; ++t) {
+    const int j = wave + NW * t;
+    const int s = j * 64 + lane;
+    const bool is_w = j >= INS_A;
+    const int r = (is_w ? s - INS_A * 64 : s) >> 3, p = s & 7;
+    const int c = p ^ ((r >> 1) & 7);
+    int row;
+    if (is_w) row = w_row_mfma<EPI, BN>(a, tn, r);
+    else row = m0 + r < a.M ? m0 + r : a.M - 1;
+    src_off[t] = row * K + c * 8;
+    src_is_w[t] = is_w;
+  }
+  const f16* Wf = reinterpret_cast<const f16*>(a.W);
+  const int8_t* W8p = reinterpret_cast<const int8_t*>(a.W);
+  int w8_off[CB8 > 0 ? CB8 : 1];
+#pragma unroll
+  for (int i = 0; i < CB8; ++i) {
+    const int q = tid + i * NT, r = q >> 2, c = q & 3;
+    w8_off[i] = w_row_mfma<EPI, BN>(a, tn, r) * K + c * 16;
+  }
+  i32x4 rw8[CB8 > 0 ? CB8 : 1];
+
+  auto issue = [&](int kt, f16* st) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int t = 0; t < LPW; ++t) {
+      const int j = wave + NW * t;
+      const f16* g = (src_is_w[t] ? Wf : A) + src_off[t] + k0;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)(st + j * 512), 16, 0, 0);
+    }
+    if constexpr (W8) {
+#pragma unroll
+      for (int i = 0; i < CB8; ++i) rw8[i] = *reinterpret_cast<const i32x4*>(W8p + w8_off[i] + k0);
+    }
+  };
+  auto store_w8 = [&](f16* st) {
+#pragma unroll
+    for (int i = 0; i < CB8; ++i) {
+      const int q = tid + i * NT, r = q >> 2, c = q & 3;
+      *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c)) = i8x8_to_f16x8(rw8[i][0], rw8[i][1]);
+      *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c + 1)) = i8x8_to_f16x8(rw8[i][2], rw8[i][3]);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int kt0 = split * a.kt_per_split;
+  const int kt1 = min(K / BK, kt0 + a.kt_per_split);
+  if (kt0 < kt1) {
+    issue(kt0, smem);
+    if constexpr (W8) store_w8(smem);
+  }
+  for (int kt = kt0; kt < kt1; ++kt) {
+    f16* cur = smem + ((kt - kt0) & 1) * STAGE;
+    f16* nxt = smem + ((kt - kt0 + 1) & 1) * STAGE;
+    PHI_WAIT_VMCNT(0);
+    __syncthreads();
+    const bool more = kt + 1 < kt1;
+    if (more) issue(kt + 1, nxt);
+    f16x8 af[2][TM], bf[2][TN];
+    auto ld = [&](int kk, f16x8* fa, f16x8* fb) {
+      const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(wn * WN + j * 32 + (lane & 31), c));
+    };
+    ld(0, af[0], bf[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) ld(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][i], bf[kk & 1][j], acc[i][j], 0, 0, 0);
+    }
+    // schedule: step-0 fragments, then per step the next step's fragments
+    // interleaved one read per R MFMAs with this step's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      constexpr int R = (TM * TN) / (TM + TN) > 0 ? (TM * TN) / (TM + TN) : 1;
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
+        }
+        if (TM * TN > R * (TM + TN)) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * (TM + TN), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      }
+    }
+    if constexpr (W8) {
+      if (more) store_w8(nxt);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const int grp = lane >> 5, col_l = lane & 31;
+  auto row_of = [&](int i, int v) { return m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3); };
+  float sc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    sc[j] = 1.0f;
+    if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN>(a, tn, wn * WN + j * 32 + col_l)];
+  }
+
+  if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_PARTIAL) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = tn * BN + wn * WN + j * 32 + col_l;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = row_of(i, v);
+          if (m >= a.M) continue;
+          const float y = acc[i][j][v] * sc[j];
+          if constexpr (EPI == EPI_F32) a.out[(size_t)m * a.ldo + n] = y;
+          else if constexpr (EPI == EPI_RESID) a.x[(size_t)m * a.ldx + n] += y;
+          else a.out[((size_t)split * a.M + m) * a.N + n] = y;
+        }
+    }
+  } else if constexpr (EPI == EPI_SILU) {
+    f16* act = reinterpret_cast<f16*>(a.act);
+#pragma unroll
+    for (int p = 0; p < TN / 2; ++p) {
+      const int n = tn * (BN / 2) + wn * (WN / 2) + p * 32 + col_l;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = row_of(i, v);
+          if (m >= a.M) continue;
+          act[(size_t)m * a.ld_act + n] = (f16)silu_mul(acc[i][2 * p][v] * sc[2 * p], acc[i][2 * p + 1][v] * sc[2 * p + 1]);
+        }
+    }
+  } else {  // EPI_QKV
+    const int col0 = tn * BN + wn * 96;  // first fused row of this wave's head
+    if (col0 >= a.N) return;
+    const int q_end = a.nh * 96, k_end = (a.nh + a.nkv) * 96;
+    const bool is_v = col0 >= k_end;
+    const int head = col0 < q_end ? col0 / 96 : (col0 < k_end ? (col0 - q_end) / 96 : (col0 - k_end) / 96);
+    const int nheads = col0 < q_end ? a.nh : a.nkv;
+    f16* dst = reinterpret_cast<f16*>(col0 < q_end ? a.q : a.k);
+    f16* vt = reinterpret_cast<f16*>(a.vt);
+    const int d0 = col_l, d1 = 48 + col_l, d2 = col_l < 16 ? 32 + col_l : 64 + col_l;
+    const int f2 = 32 + (col_l & 15);  // frequency index of the third block's pair
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = row_of(i, v);
+        const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1], y2 = acc[i][2][v] * sc[2];
+        const float y2p = __shfl_xor(y2, 16);  // partner of the third block (all lanes take part)
+        if (m >= a.M) continue;
+        const int b = m / a.S, s = m - b * a.S;
+        if (is_v) {
+          f16* base = vt + ((size_t)(b * a.nkv + head) * 96) * a.s_pad + s;
+          base[(size_t)d0 * a.s_pad] = (f16)y0;
+          base[(size_t)d1 * a.s_pad] = (f16)y1;
+          base[(size_t)d2 * a.s_pad] = (f16)y2;
+        } else {
+          const float c0 = a.rope_cos[(size_t)s * 48 + col_l], s0 = a.rope_sin[(size_t)s * 48 + col_l];
+          const float c2 = a.rope_cos[(size_t)s * 48 + f2], s2 = a.rope_sin[(size_t)s * 48 + f2];
+          f16* base = dst + ((size_t)(b * nheads + head) * a.S + s) * 96;
+          base[d0] = (f16)(y0 * c0 - y1 * s0);
+          base[d1] = (f16)(y1 * c0 + y0 * s0);
+          base[d2] = (f16)(col_l < 16 ? y2 * c2 - y2p * s2 : y2 * c2 + y2p * s2);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 core
+template <int BN>
+__device__ __forceinline__ int w_row_simt(const GemmArgs& a, int tn, int r, int epi) {
+  if (epi == EPI_SILU) {
+    constexpr int H2 = BN / 2;
+    const int I = a.N >> 1;
+    return r < H2 ? tn * H2 + r : I + tn * H2 + (r - H2);
+  }
+  const int n = tn * BN + r;
+  return n < a.N ? n : a.N - 1;
+}
+
 template <class AT>
 __device__ __forceinline__ void store8(AT* p, const float* v);
-template <>
-__device__ __forceinline__ void store8<f16>(f16* p, const float* v) {
-  *reinterpret_cast<f16x8*>(p) =
-      f16x8{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3], (f16)v[4], (f16)v[5], (f16)v[6], (f16)v[7]};
-}
 template <>
 __device__ __forceinline__ void store8<float>(float* p, const float* v) {
   reinterpret_cast<f32x4*>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
   reinterpret_cast<f32x4*>(p)[1] = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-// Epilogue over an fp32 tile sC[BM][ldc] whose origin is row m0, N-tile tn.
-template <int EPI, class AT, int BM, int BN>
-__device__ void gemm_epilogue(const float* sC, int ldc, int m0, int tn, const GemmArgs& a, int tid, int nt) {
+// Epilogue over an fp32 tile sC[BM][ldc] (origin row m0, N-tile tn), float32 model.
+template <int EPI, int BM, int BN>
+__device__ void simt_epilogue(const float* sC, int ldc, int m0, int tn, const GemmArgs& a, int tid, int nt) {
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID) {
     const int n0 = tn * BN;
     for (int u = tid; u < BM * (BN / 4); u += nt) {
@@ -93,7 +369,7 @@ __device__ void gemm_epilogue(const float* sC, int ldc, int m0, int tn, const Ge
   } else if constexpr (EPI == EPI_SILU) {
     constexpr int H2 = BN / 2;
     const int n0 = tn * H2;
-    AT* act = reinterpret_cast<AT*>(a.act);
+    float* act = reinterpret_cast<float*>(a.act);
     for (int u = tid; u < BM * (H2 / 4); u += nt) {
       const int r = u / (H2 / 4), c = (u % (H2 / 4)) * 4;
       const int m = m0 + r;
@@ -102,213 +378,59 @@ __device__ void gemm_epilogue(const float* sC, int ldc, int m0, int tn, const Ge
       const f32x4 up = *reinterpret_cast<const f32x4*>(sC + r * ldc + H2 + c);
       f32x4 y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = g[e] / (1.0f + __expf(-g[e])) * up[e];
-      vec4<AT>::store(act + (size_t)m * a.ld_act + n0 + c, y);
+      for (int e = 0; e < 4; ++e) y[e] = silu_mul(g[e], up[e]);
+      vec4<float>::store(act + (size_t)m * a.ld_act + n0 + c, y);
     }
-  } else {  // EPI_QKV
-    const int hd = a.hd, half = hd >> 1;
-    const int n0 = tn * BN;
-    constexpr int kHeads = BN / 96;  // head_dim 96: tiles hold whole heads
+  } else {  // EPI_QKV, one 96-wide head per tile
+    const int hd = 96, half = 48;
+    const int col0 = tn * BN;
     const int q_end = a.nh * hd, k_end = (a.nh + a.nkv) * hd;
-    AT* qo = reinterpret_cast<AT*>(a.q);
-    AT* ko = reinterpret_cast<AT*>(a.k);
-    AT* vo = reinterpret_cast<AT*>(a.vt);
-    const int per_row = kHeads * (half / 4);
-    for (int u = tid; u < BM * per_row; u += nt) {
-      const int r = u / per_row, rest = u % per_row;
-      const int hh = rest / (half / 4), d = (rest % (half / 4)) * 4;
-      const int m = m0 + r, col0 = n0 + hh * hd;
-      if (m >= a.M || col0 >= k_end) continue;
-      AT* dst;
-      int head, nheads;
-      if (col0 < q_end) { dst = qo; head = col0 / hd; nheads = a.nh; }
-      else { dst = ko; head = (col0 - q_end) / hd; nheads = a.nkv; }
-      const int b = m / a.S, s = m - b * a.S;
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sC + r * ldc + hh * hd + d);
-      const f32x4 x2 = *reinterpret_cast<const f32x4*>(sC + r * ldc + hh * hd + half + d);
-      const f32x4 cs = vec4<float>::load(a.rope_cos + (size_t)s * half + d);
-      const f32x4 sn = vec4<float>::load(a.rope_sin + (size_t)s * half + d);
-      AT* base = dst + ((size_t)(b * nheads + head) * a.S + s) * hd;
-      vec4<AT>::store(base + d, x1 * cs - x2 * sn);
-      vec4<AT>::store(base + half + d, x2 * cs + x1 * sn);
-    }
-    // V heads, transposed: each unit writes 8 consecutive positions of one d.
-    const int per_head = hd * (BM / 8);
-    for (int u = tid; u < kHeads * per_head; u += nt) {
-      const int hh = u / per_head, rest = u % per_head;
-      const int d = rest / (BM / 8), rg = (rest % (BM / 8)) * 8;
-      const int col0 = n0 + hh * hd;
-      if (col0 < k_end || col0 >= a.N) continue;
+    if (col0 >= a.N) return;
+    float* qo = reinterpret_cast<float*>(a.q);
+    float* ko = reinterpret_cast<float*>(a.k);
+    float* vo = reinterpret_cast<float*>(a.vt);
+    if (col0 < k_end) {
+      float* dst = col0 < q_end ? qo : ko;
+      const int head = col0 < q_end ? col0 / hd : (col0 - q_end) / hd;
+      const int nheads = col0 < q_end ? a.nh : a.nkv;
+      for (int u = tid; u < BM * (half / 4); u += nt) {
+        const int r = u / (half / 4), d = (u % (half / 4)) * 4;
+        const int m = m0 + r;
+        if (m >= a.M) continue;
+        const int b = m / a.S, s = m - b * a.S;
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(sC + r * ldc + d);
+        const f32x4 x2 = *reinterpret_cast<const f32x4*>(sC + r * ldc + half + d);
+        const f32x4 cs = vec4<float>::load(a.rope_cos + (size_t)s * half + d);
+        const f32x4 sn = vec4<float>::load(a.rope_sin + (size_t)s * half + d);
+        float* base = dst + ((size_t)(b * nheads + head) * a.S + s) * hd;
+        vec4<float>::store(base + d, x1 * cs - x2 * sn);
+        vec4<float>::store(base + half + d, x2 * cs + x1 * sn);
+      }
+    } else {
       const int head = (col0 - k_end) / hd;
-      const int mf = m0 + rg;
-      if (mf >= a.M) continue;
-      const int bf = mf / a.S, sf = mf - bf * a.S;
-      float v[8];
+      for (int u = tid; u < hd * (BM / 8); u += nt) {
+        const int d = u / (BM / 8), rg = (u % (BM / 8)) * 8;
+        const int mf = m0 + rg;
+        if (mf >= a.M) continue;
+        const int bf = mf / a.S, sf = mf - bf * a.S;
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sC[(rg + e) * ldc + hh * hd + d];
-      if (mf + 7 < a.M && sf + 7 < a.S && (sf & 7) == 0) {
-        store8<AT>(vo + ((size_t)(bf * a.nkv + head) * hd + d) * a.s_pad + sf, v);
-      } else {
-        for (int e = 0; e < 8; ++e) {
-          const int m = mf + e;
-          if (m >= a.M) break;
-          const int b = m / a.S, s = m - b * a.S;
-          vo[((size_t)(b * a.nkv + head) * hd + d) * a.s_pad + s] = from_f32<AT>(v[e]);
+        for (int e = 0; e < 8; ++e) v[e] = sC[(rg + e) * ldc + d];
+        if (mf + 7 < a.M && sf + 7 < a.S && (sf & 7) == 0) {
+          store8<float>(vo + ((size_t)(bf * a.nkv + head) * hd + d) * a.s_pad + sf, v);
+        } else {
+          for (int e = 0; e < 8; ++e) {
+            const int m = mf + e;
+            if (m >= a.M) break;
+            const int b = m / a.S, s = m - b * a.S;
+            vo[((size_t)(b * a.nkv + head) * hd + d) * a.s_pad + s] = v[e];
+          }
         }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- MFMA core
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
-
-__device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
-  f16x8 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[e] = (f16)(float)(int8_t)(lo >> (8 * e));
-    o[4 + e] = (f16)(float)(int8_t)(hi >> (8 * e));
-  }
-  return o;
-}
-
-template <int BM, int BN, int WGM, int WGN, bool W8, int EPI>
-__global__ __launch_bounds__(WGM* WGN * 64) void phi_gemm_mfma_kernel(GemmArgs a) {
-  constexpr int NT = WGM * WGN * 64;
-  constexpr int BK = 64;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int STAGE = (BM + BN) * BK;  // f16 elements per stage
-  constexpr int LDC = BN + 4;
-  constexpr int SMEM = (2 * STAGE * 2 > BM * LDC * 4) ? 2 * STAGE * 2 : BM * LDC * 4;
-  constexpr int CA = BM * 8 / NT;                      // A chunks per thread
-  constexpr int CB = W8 ? BN * 4 / NT : BN * 8 / NT;   // W chunks per thread
-  static_assert(CA * NT == BM * 8 && (W8 ? CB * NT == BN * 4 : CB * NT == BN * 8), "tile/threads");
-  static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
-
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  f16* stage0 = reinterpret_cast<f16*>(smem);
-
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  if (tile >= a.tiles_m * a.tiles_n) return;
-  const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
-  const int m0 = tm * BM;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-
-  const f16* A = reinterpret_cast<const f16*>(a.A);
-  const int K = a.K;
-
-  // per-thread global sources (row pointers fixed over the K loop)
-  const f16* a_src[CA];
-  int a_dst[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int q = tid + i * NT, r = q >> 3, c = q & 7;
-    const int gm = m0 + r < a.M ? m0 + r : a.M - 1;
-    a_src[i] = A + (size_t)gm * K + c * 8;
-    a_dst[i] = swz(r, c);
-  }
-  const char* w_src[CB];
-  int w_dst[CB];
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int q = tid + i * NT;
-    if constexpr (W8) {
-      const int r = q >> 2, c = q & 3;
-      w_src[i] = reinterpret_cast<const char*>(a.W) + (size_t)w_row<EPI, BN>(a, tn, r) * K + c * 16;
-      w_dst[i] = BM * BK + swz(r, 2 * c);  // second chunk at swz(r, 2c + 1)
-    } else {
-      const int r = q >> 3, c = q & 7;
-      w_src[i] = reinterpret_cast<const char*>(a.W) + ((size_t)w_row<EPI, BN>(a, tn, r) * K + c * 8) * 2;
-      w_dst[i] = BM * BK + swz(r, c);
-    }
-  }
-
-  i32x4 ra[CA], rw[CB];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const i32x4*>(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      rw[i] = *reinterpret_cast<const i32x4*>(w_src[i] + (W8 ? k0 : k0 * 2));
-  };
-  auto lstore = [&](f16* st) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<i32x4*>(st + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      if constexpr (W8) {
-        const int q = tid + i * NT, r = q >> 2, c = q & 3;
-        *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c)) = i8x8_to_f16x8(rw[i][0], rw[i][1]);
-        *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c + 1)) = i8x8_to_f16x8(rw[i][2], rw[i][3]);
-      } else {
-        *reinterpret_cast<i32x4*>(st + w_dst[i]) = rw[i];
-      }
-    }
-  };
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
-
-  const int nk = K / BK;
-  gload(0);
-  lstore(stage0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    f16* cur = stage0 + (kt & 1) * STAGE;
-    f16* nxt = stage0 + ((kt + 1) & 1) * STAGE;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      f16x8 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const f16x8*>(cur + swz(r, c));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, c));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(nxt);
-    __syncthreads();
-  }
-
-  // accumulators -> LDS tile (row = 8 (v / 4) + 4 (lane / 32) + v % 4, col = lane % 32)
-  float* sC = reinterpret_cast<float*>(smem);
-  const f16* sc16 = reinterpret_cast<const f16*>(a.scale);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = wn * WN + j * 32 + (lane & 31);
-    float s = 1.0f;
-    if constexpr (W8) s = (float)sc16[w_row<EPI, BN>(a, tn, col)];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        sC[row * LDC + col] = acc[i][j][v] * s;
-      }
-    }
-  }
-  __syncthreads();
-  gemm_epilogue<EPI, f16, BM, BN>(sC, LDC, m0, tn, a, tid, NT);
-}
-
-// ---------------------------------------------------------------- fp32 core
 template <int BN, int EPI>
 __global__ __launch_bounds__(256) void phi_gemm_simt_f32_kernel(GemmArgs a) {
   constexpr int BM = 32, BK = 32, NT = 256;
@@ -337,7 +459,7 @@ __global__ __launch_bounds__(256) void phi_gemm_simt_f32_kernel(GemmArgs a) {
     }
     for (int q = tid; q < BN * 8; q += NT) {
       const int rw = q >> 3, cw = (q & 7) * 4;
-      const f32x4 v = vec4<float>::load(W + (size_t)w_row<EPI, BN>(a, tn, rw) * a.K + k0 + cw);
+      const f32x4 v = vec4<float>::load(W + (size_t)w_row_simt<BN>(a, tn, rw, EPI) * a.K + k0 + cw);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sW[rw][cw + e] = v[e];
     }
@@ -353,7 +475,7 @@ __global__ __launch_bounds__(256) void phi_gemm_simt_f32_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < BN / 8; ++j) sC[r * LDC + cl + 8 * j] = acc[j];
   __syncthreads();
-  gemm_epilogue<EPI, float, BM, BN>(sC, LDC, m0, tn, a, tid, NT);
+  simt_epilogue<EPI, BM, BN>(sC, LDC, m0, tn, a, tid, NT);
 }
 
 }  // namespace phi

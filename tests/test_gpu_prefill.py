@@ -173,6 +173,9 @@ def test_mini_prefix_invariance_and_determinism(phi, mini_f16):
     a = _run(phi, wl.cfg, mini_f16[1], ids)
     b = _run(phi, wl.cfg, mini_f16[1], ids)
     assert np.array_equal(a, b)
+    # a shorter prefix may take other GEMM tile shapes and K splits (the plan
+    # depends on the token count), so it sums in another order: equal to
+    # within fp32 rounding, same argmax wherever the top-2 gap exceeds 1e-3
     c = _run(phi, wl.cfg, mini_f16[1], ids[:, :200])
-    cos = parity.row_cosines(c[0], a[0, :200])
-    assert cos.min() > 1 - 1e-9
+    s = parity.summary(c[0], a[0, :200])
+    assert s["min_cos"] > 1 - 1e-6 and not s["failures"], s
