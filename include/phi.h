@@ -64,7 +64,7 @@ typedef enum phi_wtype { PHI_WT_F32 = 0, PHI_WT_F16 = 1, PHI_WT_I8 = 2 } phi_wty
 
 typedef struct phi_config {
   int32_t n_layers;
-  int32_t hidden;       /* H; multiple of 64                                  */
+  int32_t hidden;       /* H; multiple of 64, at most 4096                    */
   int32_t n_heads;      /* query heads                                        */
   int32_t n_kv_heads;   /* divides n_heads (n_kv_heads == n_heads: MHA)       */
   int32_t head_dim;     /* 96 ([P1] section 2)                                */

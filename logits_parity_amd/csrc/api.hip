@@ -151,7 +151,8 @@ bool check_config(const phi_config* c) {
   return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && c->head_dim == 96 &&
          c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
          (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 128 && c->intermediate % 128 == 0 &&
-         c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 && c->max_pos <= kMaxPos;
+         c->hidden <= 4 * 4 * kNormThreads && c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 &&
+         c->max_pos <= kMaxPos;
 }
 
 // ---------------------------------------------------------------- GEMM dispatch
@@ -198,8 +199,13 @@ phi_status attention(bool f32, AttnArgs a, int batch, hipStream_t st) {
     hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
     return launched();
   }
-  // more queries per workgroup when there are enough workgroups to fill the chip
+  // more queries per workgroup when there are enough workgroups to fill the
+  // chip; otherwise 32 queries per workgroup with the keys split over 4 waves
   const long units = (long)batch * a.nh;
+  if (units * ((a.S + 127) / 128) < 512) {
+    hipLaunchKernelGGL(phi_attn_prefill_split_kernel<4>, dim3((a.S + 31) / 32, a.nh, batch), dim3(256), 0, st, a);
+    return launched();
+  }
   if (units * ((a.S + 127) / 128) >= 512)
     hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<4>, dim3((a.S + 127) / 128, a.nh, batch), dim3(256), 0, st, a);
   else if (units * ((a.S + 63) / 64) >= 256)
@@ -211,9 +217,8 @@ phi_status attention(bool f32, AttnArgs a, int batch, hipStream_t st) {
 
 template <class ET, class AT>
 phi_status norm(bool embed, NormArgs a, hipStream_t st) {
-  const dim3 grid((a.T + 3) / 4);
-  if (embed) hipLaunchKernelGGL((phi_norm_embed_kernel<ET, AT>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((phi_norm_rms_kernel<ET, AT>), grid, dim3(256), 0, st, a);
+  if (embed) hipLaunchKernelGGL((phi_norm_kernel<ET, AT, true>), dim3(a.T), dim3(kNormThreads), 0, st, a);
+  else hipLaunchKernelGGL((phi_norm_kernel<ET, AT, false>), dim3(a.T), dim3(kNormThreads), 0, st, a);
   return launched();
 }
 
@@ -335,16 +340,17 @@ struct DecodePlan {
   size_t off_ml, total;
 };
 
+// Splits of whole 64-token chunks per wave (16 pages per workgroup round):
+// 32 pages per split unless that leaves fewer than ~2 workgroups per CU.
 DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
   DecodePlan p;
   const int np = (max_ctx + 15) / 16;
   const long units = (long)batch * n_kv_heads;
-  int want = (int)((2048 + units - 1) / units);  // about 8 workgroups per CU
-  const int max_split = (np + 3) / 4;            // at least 4 pages (one per wave) per split
-  if (want > max_split) want = max_split;
-  if (want < 1) want = 1;
-  p.pages_per_split = (np + want - 1) / want;
-  p.n_split = (np + p.pages_per_split - 1) / p.pages_per_split;
+  int pps = 32;
+  if (units * ((np + pps - 1) / pps) < 512) pps = 16;
+  if (pps > (np + 15) / 16 * 16) pps = (np + 15) / 16 * 16;
+  p.pages_per_split = pps;
+  p.n_split = (np + pps - 1) / pps;
   const size_t parts = (size_t)batch * n_q_heads * p.n_split;
   p.off_ml = round_up(parts * 128 * 4, 256);
   p.total = p.off_ml + round_up(parts * 2 * 4, 256);

@@ -3,16 +3,21 @@
 //
 // Split kernel: a workgroup owns one (sequence, KV head, context split) and
 // serves all G query heads of the GQA group from one read of each K/V page.
-// Its 4 waves take pages round-robin.  Inside a wave, lane l owns token slot
-// l / 4 of the page and dims 32 (l % 4) .. +31: it reads 64 contiguous bytes
-// of K and 32 of V per page, forms partial q.k with v_dot2_f32_f16, and two
-// xor-shuffles complete each dot product.  Every lane keeps its own online
-// softmax state (max, sum, 32-wide output per head) over the tokens it has
-// seen, so no cross-lane traffic is needed per page; states are merged by
-// log-sum-exp once at the end (shuffles across the 16 token lanes, then LDS
-// across the 4 waves).  E4M3 bytes are decoded with the hardware
-// v_cvt_pk_f32_fp8; the per-head scale multiplies the final output once.
-// The split writes (o unnormalised, max, sum) to the workspace.
+// Its 4 waves take chunks of 4 pages (64 tokens) round-robin.  Per chunk a wave
+//  1. forms the scores S^T[token][head] = K Q^T with v_mfma_f32_16x16x32_f16:
+//     one page is 16 tokens x 128 dims, so 4 MFMAs per page; lane l supplies
+//     key row l % 16 and dims 8 (l / 16) + 32 k straight from the page, and
+//     the query of head l % 16 (zero for l % 16 >= G) as the other operand;
+//  2. updates one running max per head for the whole wave (so the output is
+//     rescaled once per chunk) and the probabilities p = 2^(s - max);
+//  3. passes p through a per-wave LDS slot into the layout of the value pass;
+//  4. accumulates o[h][d] += p[h][t] v[t][d] on the VALU: lane l owns dims
+//     16 (l % 8) .. +15 and tokens l / 8 + 8 j of the chunk, reading 16 bytes
+//     of E4M3 per token and decoding them with v_cvt_pk_f32_fp8.
+// At the end the lanes' partial outputs are summed (they share the running
+// max), the 4 waves are merged by log-sum-exp through LDS, and the split's
+// (o unnormalised, max, sum) go to the workspace.  The per-head value scale
+// multiplies the final output once.
 //
 // Merge kernel: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m) * scale.
 #pragma once
@@ -34,113 +39,159 @@ struct DecodeArgs {
   float scale_log2;  // sm_scale * log2(e)
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 template <int G>
 __global__ __launch_bounds__(256) void phi_decode_split_kernel(DecodeArgs a) {
-  constexpr int D = 128, PG = 16;
+  constexpr int D = 128, PG = 16, CH = 4;  // pages per chunk
+  static_assert(G >= 1 && G <= 8, "GQA group");
+  __shared__ float sP[4][CH * PG][G];      // per wave: probabilities of the chunk
   __shared__ float s_o[4][G][D];
   __shared__ float s_ml[4][G][2];
   __shared__ int s_err[4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t = lane >> 2, dq = lane & 3;
+  const int hl = lane & 15, kq = lane >> 4;      // score layout: head column, token quad
+  const int dq = lane & 7, t8 = lane >> 3;       // value layout: dims 16 dq.., tokens t8 + 8 j
   const int L = a.ctx_lens[b];
   bool err = L < 1 || L > a.max_pages * PG;
   const int np = err ? 0 : (L + PG - 1) / PG;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(np, p_begin + a.pages_per_split);
-
-  f16x2 qv[G][16];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const f16* qp = a.q + ((size_t)b * a.Hq + g * G + h) * D + dq * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(qp + i * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qv[h][i * 4 + e] = f16x2{v[2 * e], v[2 * e + 1]};
-    }
-  }
-  float m[G], l[G], o[G][32];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -__builtin_inff();
-    l[h] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) o[h][d] = 0.f;
-  }
-
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-  for (int p = p_begin + w; p < p_end; p += 4) {
-    const int phys = bt[p];
-    if (phys < 0 || phys >= a.n_pages) { err = true; break; }
-    const size_t off = ((size_t)(phys * a.Hkv + g) * PG + t) * D + dq * 32;
-    const f16x8* kp = reinterpret_cast<const f16x8*>(a.k_pool + off);
-    const i32x4* vp = reinterpret_cast<const i32x4*>(a.v_pool + off);
-    f16x8 kv[4];
+
+  // query operand: head hl (zero beyond the group), dims 32 k + 8 kq .. +7
+  f16x8 qf[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kv[i] = kp[i];
-    const i32x4 vb0 = vp[0], vb1 = vp[1];
-    float s[G];
+  for (int k = 0; k < 4; ++k) {
+    if (hl < G) qf[k] = *reinterpret_cast<const f16x8*>(a.q + ((size_t)b * a.Hq + g * G + hl) * D + 32 * k + 8 * kq);
+    else qf[k] = f16x8{};
+  }
+
+  float o[G][16];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int d = 0; d < 16; ++d) o[h][d] = 0.f;
+  float m_run = -__builtin_inff();  // lanes hl < G: running max of head hl
+  float l_run = 0.f;                // lanes hl < G: partial sum over this lane's tokens
+
+  for (int c0 = p_begin + CH * w; c0 < p_end; c0 += CH * 4) {
+    // physical pages of the chunk; pages past the split reuse the first one (masked)
+    int phys[CH];
+    bool bad = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = __builtin_amdgcn_fdot2(qv[h][i * 4 + e], f16x2{kv[i][2 * e], kv[i][2 * e + 1]}, acc, false);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      s[h] = acc * a.scale_log2;
+    for (int pi = 0; pi < CH; ++pi) {
+      const int p = c0 + pi < p_end ? c0 + pi : c0;
+      phys[pi] = bt[p];
+      bad |= phys[pi] < 0 || phys[pi] >= a.n_pages;
     }
-    if (p * PG + t < L) {
-      float vf[32];
+    if (bad) { err = true; break; }
+
+    // 1. scores: per page, 16 tokens x 16 heads
+    f32x4 sc[CH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int wv = i < 4 ? vb0[i] : vb1[i - 4];
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
+    for (int pi = 0; pi < CH; ++pi) {
+      const f16* kp = a.k_pool + (((size_t)phys[pi] * a.Hkv + g) * PG + hl) * D + 8 * kq;
+      f16x8 kf[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kf[k] = *reinterpret_cast<const f16x8*>(kp + 32 * k);
+      sc[pi] = f32x4{};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sc[pi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[k], qf[k], sc[pi], 0, 0, 0);
+    }
+    // value bytes of this lane's 8 tokens (issued early, used after the softmax)
+    i32x4 vb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t8 + 8 * j;  // token within the chunk: page j / 2, slot t % 16
+      vb[j] = *reinterpret_cast<const i32x4*>(a.v_pool + (((size_t)phys[j >> 1] * a.Hkv + g) * PG + (t & 15)) * D + 16 * dq);
+    }
+
+    // 2. running max per head over the chunk; lanes hl, hl+16, hl+32, hl+48 share a head
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int pi = 0; pi < CH; ++pi)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = (c0 + pi) * PG + 4 * kq + j;
+        float s = sc[pi][j] * a.scale_log2;
+        if (c0 + pi >= p_end || tok >= L) s = -__builtin_inff();
+        sc[pi][j] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: the chunk's first token is valid
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int pi = 0; pi < CH; ++pi)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = exp2f(sc[pi][j] - m_new);
+        ps += p;
+        if (hl < G) sP[w][pi * PG + 4 * kq + j][hl] = p;
+      }
+    l_run = l_run * alpha + ps;
+    __builtin_amdgcn_wave_barrier();  // LDS writes above stay before the reads below (in-order per wave)
+
+    // 3. per-head rescale factors to every lane; probabilities of this lane's tokens
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) al[h] = __shfl(alpha, h);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[h][d] *= al[h];
+
+    // 4. o += p v
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t8 + 8 * j;
+      // slots past the context may hold any bytes (even NaN codes): skip them
+      if (c0 + (j >> 1) >= p_end || c0 * PG + t >= L) continue;
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = sP[w][t][h];
+      float vf[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vb[j][i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vb[j][i], true);
         vf[4 * i + 0] = lo[0];
         vf[4 * i + 1] = lo[1];
         vf[4 * i + 2] = hi[0];
         vf[4 * i + 3] = hi[1];
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], s[h]);
-        const float al = exp2f(m[h] - mn), pp = exp2f(s[h] - mn);
-        l[h] = l[h] * al + pp;
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int d = 0; d < 32; ++d) o[h][d] = fmaf(pp, vf[d], o[h][d] * al);
-        m[h] = mn;
-      }
+        for (int d = 0; d < 16; ++d) o[h][d] = fmaf(pv[h], vf[d], o[h][d]);
     }
   }
 
-  // merge the 16 token lanes of this wave (lane bits 2..5)
+  // lanes of one dim group share the running max: plain sums over t8
 #pragma unroll
-  for (int mask = 4; mask < 64; mask <<= 1) {
+  for (int mask = 8; mask < 64; mask <<= 1)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], mask), lo = __shfl_xor(l[h], mask);
-      const float mn = fmaxf(m[h], mo);
-      const float a1 = m[h] == -__builtin_inff() ? 0.f : exp2f(m[h] - mn);
-      const float a2 = mo == -__builtin_inff() ? 0.f : exp2f(mo - mn);
-      l[h] = l[h] * a1 + lo * a2;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 32; ++d) o[h][d] = o[h][d] * a1 + __shfl_xor(o[h][d], mask) * a2;
-      m[h] = mn;
-    }
-  }
+      for (int d = 0; d < 16; ++d) o[h][d] += __shfl_xor(o[h][d], mask);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
   const int any_err = __any(err);
-  if (lane < 4) {
+  if (lane < 8) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 32; ++d) s_o[w][h][dq * 32 + d] = o[h][d];
-      if (lane == 0) { s_ml[w][h][0] = m[h]; s_ml[w][h][1] = l[h]; }
-    }
+      for (int d = 0; d < 16; ++d) s_o[w][h][16 * dq + d] = o[h][d];
+  }
+  if (lane < G) {
+    s_ml[w][lane][0] = m_run;
+    s_ml[w][lane][1] = l_tot;
   }
   if (lane == 0) s_err[w] = any_err;
   __syncthreads();

@@ -22,66 +22,68 @@ struct NormArgs {
   float eps;
 };
 
-// x[t] = embed[ids[t]] (widened to fp32), then xn[t] = rmsnorm(x[t]) * gain.
-// An id outside [0, V) yields a NaN row in x and xn.
-template <class ET, class AT>
-__global__ __launch_bounds__(256) void phi_norm_embed_kernel(NormArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.T) return;
-  const int id = a.ids[row];
-  float* xr = a.x + (size_t)row * a.H;
-  AT* xo = reinterpret_cast<AT*>(a.xn) + (size_t)row * a.H;
-  const ET* g = reinterpret_cast<const ET*>(a.gain);
-  if (id < 0 || id >= a.V) {
-    const float nan = __builtin_nanf("");
-    for (int c = lane * 4; c < a.H; c += 256) {
-      vec4<float>::store(xr + c, f32x4{nan, nan, nan, nan});
-      vec4<AT>::store(xo + c, f32x4{nan, nan, nan, nan});
-    }
-    return;
-  }
-  const ET* e = reinterpret_cast<const ET*>(a.embed) + (size_t)id * a.H;
-  float ss = 0.f;
-  for (int c = lane * 4; c < a.H; c += 256) {
-    f32x4 v = vec4<ET>::load(e + c);
-    vec4<float>::store(xr + c, v);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-  for (int c = lane * 4; c < a.H; c += 256) {
-    f32x4 v = vec4<ET>::load(e + c);
-    f32x4 gv = vec4<ET>::load(g + c);
-    vec4<AT>::store(xo + c, v * r * gv);
-  }
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxChunks = 4;  // hidden <= 4 * 4 * 256 = 4096
+
+// Sum over the workgroup (4 waves) via LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
 }
 
-// x[t] += sum_s part[s][t] (when nsplit > 0); xn[t] = rmsnorm(x[t]) * gain.
-template <class ET, class AT>
-__global__ __launch_bounds__(256) void phi_norm_rms_kernel(NormArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.T) return;
+// One workgroup per row, up to kNormMaxChunks float4 chunks per thread held in
+// registers between the sum of squares and the scaling.
+// EMBED: x[t] = embed[ids[t]] (an id outside [0, V) gives a NaN row).
+// else:  x[t] += sum_s part[s][t] for nsplit > 0 (then written back).
+// Both: xn[t] = x[t] / sqrt(mean(x[t]^2) + eps) * gain.
+template <class ET, class AT, bool EMBED>
+__global__ __launch_bounds__(kNormThreads) void phi_norm_kernel(NormArgs a) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
   float* xr = a.x + (size_t)row * a.H;
   AT* xo = reinterpret_cast<AT*>(a.xn) + (size_t)row * a.H;
   const ET* g = reinterpret_cast<const ET*>(a.gain);
-  const size_t plane = (size_t)a.T * a.H;
+  f32x4 v[kNormMaxChunks];
   float ss = 0.f;
-  for (int c = lane * 4; c < a.H; c += 256) {
-    f32x4 v = vec4<float>::load(xr + c);
-    if (a.nsplit > 0) {
-      for (int sp = 0; sp < a.nsplit; ++sp) v += vec4<float>::load(a.part + sp * plane + (size_t)row * a.H + c);
-      vec4<float>::store(xr + c, v);
+  if constexpr (EMBED) {
+    const int id = a.ids[row];
+    const bool bad = id < 0 || id >= a.V;
+    const ET* e = reinterpret_cast<const ET*>(a.embed) + (size_t)(bad ? 0 : id) * a.H;
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < kNormMaxChunks; ++i) {
+      const int c = (tid + i * kNormThreads) * 4;
+      if (c >= a.H) break;
+      v[i] = bad ? f32x4{nan, nan, nan, nan} : vec4<ET>::load(e + c);
+      vec4<float>::store(xr + c, v[i]);
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
     }
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  } else {
+    const size_t plane = (size_t)a.T * a.H;
+#pragma unroll
+    for (int i = 0; i < kNormMaxChunks; ++i) {
+      const int c = (tid + i * kNormThreads) * 4;
+      if (c >= a.H) break;
+      v[i] = vec4<float>::load(xr + c);
+      if (a.nsplit > 0) {
+        for (int sp = 0; sp < a.nsplit; ++sp)
+          v[i] += vec4<float>::load(a.part + sp * plane + (size_t)row * a.H + c);
+        vec4<float>::store(xr + c, v[i]);
+      }
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
   }
-  ss = wave_sum(ss);
+  ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)a.H + a.eps);
-  for (int c = lane * 4; c < a.H; c += 256) {
-    f32x4 v = vec4<float>::load(xr + c);
-    f32x4 gv = vec4<ET>::load(g + c);
-    vec4<AT>::store(xo + c, v * r * gv);
+#pragma unroll
+  for (int i = 0; i < kNormMaxChunks; ++i) {
+    const int c = (tid + i * kNormThreads) * 4;
+    if (c >= a.H) break;
+    vec4<AT>::store(xo + c, v[i] * r * vec4<ET>::load(g + c));
   }
 }
 
