@@ -36,6 +36,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(profile: str, source: str):
+    """HBM-side bytes per launch from a committed counter summary, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
+        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+        if fields.get("kernel_source_sha256", "").strip() != digest:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def prefill_flops(cfg, batch, seq) -> float:
     n_lin = sum(n * k for n, k in cfg.linear_shapes().values()) * cfg.n_layers + cfg.vocab * cfg.hidden
     attn = cfg.n_layers * batch * 4 * cfg.n_heads * cfg.head_dim * seq * (seq + 1) / 2
@@ -139,6 +154,8 @@ def main():
     ap.add_argument("--cpu-positions", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no multi-GPU mode",
@@ -165,6 +182,14 @@ def main():
     workspace = torch.empty(model.workspace_bytes(wl.batch, wl.seq), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
+    if args.copy_probe_mb:
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
         model.prefill_logits(ids, logits, workspace, stream)
@@ -188,8 +213,11 @@ def main():
     log("bench: dominant kernel")
     avg_s, kflops = time_gate_up(phi, torch, dev, cfg, tokens)
     ach = kflops / avg_s / 1e12
+    traffic = None
+    if args.workload == "mini_f16_1x512":
+        traffic = measured_traffic("gate_up_gemm_mini_f16_1x512_traffic.md", "logits_parity_amd/csrc/gemm.hpp")
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
             "kernel": "phi_gemm_mfma_kernel<EPI_SILU> (fused gate/up + SiLU*up)",
             "avg_launch_us": round(avg_s * 1e6, 2), "flops_per_launch": kflops}
 
