@@ -34,6 +34,59 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+_E4M3_FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.int64)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """OCP E4M3FN code of each value: the nearest finite E4M3 value, ties to
+    the code with an even mantissa, magnitudes beyond 448 saturating to +-448.
+    (Written as a search over the 254 finite codes, so it is plainly the
+    definition; a result of zero keeps the sign of the input, as IEEE rounding
+    does.)  NaN encodes as 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1)
+    vals = E4M3_TABLE[_E4M3_FINITE]
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat):
+        if np.isnan(v):
+            out[i] = 0x7F
+            continue
+        a = min(abs(v), 448.0)
+        d = np.abs(vals - np.copysign(a, v))
+        best = np.flatnonzero(d == d.min())
+        codes = _E4M3_FINITE[best]
+        if len(codes) > 1:
+            even = codes[(codes & 1) == 0]
+            codes = even if len(even) else codes
+        c = int(codes[0])
+        if E4M3_TABLE[c] == 0.0:
+            c = 0x80 if np.signbit(v) else 0x00
+        out[i] = c
+    return out.reshape(x.shape)
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, v_scale, block_table, positions):
+    """Write token positions[b] of every sequence: K as given (binary16), V as
+    the E4M3 code of the fp32 quotient v / v_scale[g] (the same fp32 rounding
+    the kernel performs before choosing the code).  A sequence whose position
+    or page id falls outside the table or the pool is left unwritten.  Returns
+    new pools."""
+    k_pool, v_pool = k_pool.copy(), v_pool.copy()
+    B, Hkv, D = k_new.shape
+    page = k_pool.shape[2]
+    for b in range(B):
+        p = int(positions[b])
+        if not 0 <= p < block_table.shape[1] * page:
+            continue
+        phys = int(block_table[b][p // page])
+        if not 0 <= phys < k_pool.shape[0]:
+            continue
+        q = (v_new[b].astype(np.float32) / v_scale.astype(np.float32)[:, None]).astype(np.float32)
+        k_pool[phys, :, p % page, :] = k_new[b]
+        v_pool[phys, :, p % page, :] = e4m3_encode(q)
+    return k_pool, v_pool
+
+
 def gather_sequence(pool: np.ndarray, block_table_row: np.ndarray, ctx_len: int) -> np.ndarray:
     """Logical token t of a sequence lives in physical page block_table[t // page],
     slot t % page.  pool [P, Hkv, page, D] -> [ctx_len, Hkv, D]."""

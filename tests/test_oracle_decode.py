@@ -88,3 +88,50 @@ def test_kv_pool_slots_match_the_page():
     for page in (8, 32, 64):
         assert (decode.kv_pool_slots(*args, 2, 1, page), decode.kv_pool_slots(*args, 2, 2, page)) != \
             (g["k16v8_slots"], g["fp16_slots"])
+
+
+def test_e4m3_encoder_is_nearest_even_and_matches_torch():
+    from synth import to_e4m3
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(3000) * np.exp(rng.uniform(-10, 6, 3000))).astype(np.float32)
+    ties = (decode.E4M3_TABLE[[0x38, 0x39, 0x01, 0x02, 0x70, 0x71]] +
+            decode.E4M3_TABLE[[0x39, 0x3A, 0x02, 0x03, 0x71, 0x72]]) / 2
+    x = np.concatenate([x, ties, -ties, [0.0, -0.0, 448.0, 460.0, 1e6, -1e6, 2.0 ** -10, 3 * 2.0 ** -11]]).astype(np.float32)
+    ours = decode.e4m3_encode(x)
+    # an independent encoder (the input generator's, written from IEEE bit fields)
+    assert np.array_equal(ours, to_e4m3(x.astype(np.float64)))
+    # torch rounds in-range values the same way (it maps overflow to NaN, so compare in range)
+    inr = np.abs(x) < 448
+    ref = torch.from_numpy(x[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours[inr], ref)
+    # ties resolved to the even code; saturation, infinities and NaN
+    assert decode.e4m3_encode(np.array([1.0625]))[0] == 0x38
+    assert list(decode.e4m3_encode(np.array([np.inf, -np.inf, 464.0, -1e30, np.nan]))) == [0x7E, 0xFE, 0x7E, 0xFE, 0x7F]
+
+
+def test_kv_append_then_decode_reads_the_token():
+    wl = synth.DecodeWorkload("t", batch=2, ctx=40, n_q_heads=4, n_kv_heads=2, head_dim=128)
+    d = synth.decode_inputs(wl, ctx_lens=[33, 20])
+    kn = synth.normal(5, "kn", (2, 2, 128), 1.0, np.float16)
+    vn = synth.normal(5, "vn", (2, 2, 128), 1.0, np.float16)
+    kp, vp = decode.kv_append(d.k_pool, d.v_pool, kn, vn, d.v_scale, d.block_table, np.array([33, 20]))
+    for b, p in ((0, 33), (1, 20)):
+        page = d.block_table[b, p // 16]
+        assert np.array_equal(kp[page, :, p % 16], kn[b])
+        dec = decode.e4m3_decode(vp[page, :, p % 16]) * d.v_scale[:, None]
+        assert np.all(np.abs(dec - vn[b].astype(np.float64)) <= 0.07 * np.abs(vn[b].astype(np.float64)) + d.v_scale[:, None] * 2.0 ** -9)
+    # nothing else changed
+    mask = np.ones(kp.shape[:3], bool)
+    mask[d.block_table[0, 2], :, 1] = False
+    mask[d.block_table[1, 1], :, 4] = False
+    assert np.array_equal(kp[mask], d.k_pool[mask]) and np.array_equal(vp[mask], d.v_pool[mask])
+
+
+def test_kv_append_skips_out_of_range_slots():
+    wl = synth.DecodeWorkload("t", batch=3, ctx=40, n_q_heads=2, n_kv_heads=1, head_dim=128)
+    d = synth.decode_inputs(wl, ctx_lens=[10, 10, 10])
+    kn = synth.normal(6, "kn", (3, 1, 128), 1.0, np.float16)
+    bt = d.block_table.copy()
+    bt[1, 0] = wl.n_pages           # page id past the pool
+    kp, vp = decode.kv_append(d.k_pool, d.v_pool, kn, kn, d.v_scale, bt, np.array([-1, 3, bt.shape[1] * 16]))
+    assert np.array_equal(kp, d.k_pool) and np.array_equal(vp, d.v_pool)
