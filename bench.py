@@ -8,10 +8,12 @@ in HBM before the timed region.  Printed as one JSON line:
 
   value         prefill tokens/s (batch * seq * steps / wall time of the
                 timed steps, bracketed by device synchronisation)
-  roofline      the dominant kernel (fused gate/up GEMM + SiLU*up), timed
-                live with HIP events on its launch stream at the forward's
-                shape, cycling through the 32 layers' weights; algorithmic
-                flops 2 * T * 2I * H per launch against the f16 MFMA peak
+  roofline      the dominant kernel (fused gate/up GEMM + SiLU*up): its
+                launches inside forwards run right after the timed steps,
+                timed by HIP events the library records around each launch
+                on the forward's stream; algorithmic flops 2 * T * 2I * H per
+                launch against the f16 MFMA peak; HBM traffic per launch from
+                the committed counter summary (null if the kernel changed)
   decode        K16/V8 decode attention per call at the two Phi-4 shapes,
                 algorithmic bytes per call against HBM bandwidth
   cpu_baseline  the fp64 oracle on the host, on the first positions of the
@@ -57,24 +59,15 @@ def prefill_flops(cfg, batch, seq) -> float:
     return 2.0 * n_lin * batch * seq + attn
 
 
-def time_gate_up(phi, torch, dev, cfg, T, reps=64):
-    """Average duration of the fused gate/up + SiLU GEMM kernel at the forward's shape."""
-    a = torch.randn((T, cfg.hidden), device="cuda").to(torch.float16)
-    act = torch.empty((T, cfg.intermediate), dtype=torch.float16, device="cuda")
-    ws = [lw["gate_up"] for lw in dev["layers"]]
-    stream = torch.cuda.current_stream()
-    for i in range(8):
-        phi.phi_gate_up_silu(a, ws[i % len(ws)], out=act, stream=stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(reps):
-        phi.phi_gate_up_silu(a, ws[i % len(ws)], out=act, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    avg_s = e0.elapsed_time(e1) / 1e3 / reps
-    flops = 2.0 * T * 2 * cfg.intermediate * cfg.hidden
-    return avg_s, flops
+def profile_forwards(model, ids, logits, workspace, stream, n):
+    """Per-stage device time over n forwards, from HIP events that the library
+    records around each of its launches on the forward's stream."""
+    model.profile_enable(True)
+    for _ in range(n):
+        model.prefill_logits(ids, logits, workspace, stream)
+    prof = model.profile_read()
+    model.profile_enable(False)
+    return prof
 
 
 def decode_bytes(wl) -> int:
@@ -210,16 +203,22 @@ def main():
     gpu_logits = logits.cpu().numpy()
     finite = bool(np.isfinite(gpu_logits).all())
 
-    log("bench: dominant kernel")
-    avg_s, kflops = time_gate_up(phi, torch, dev, cfg, tokens)
+    log("bench: per-stage device time inside forwards")
+    n_prof = min(args.steps, 10)
+    prof = profile_forwards(model, ids, logits, workspace, stream, n_prof)
+    gu_ms, gu_n = prof["gate_up"]
+    avg_s = gu_ms / 1e3 / gu_n
+    kflops = 2.0 * tokens * 2 * cfg.intermediate * cfg.hidden
     ach = kflops / avg_s / 1e12
     traffic = None
     if args.workload == "mini_f16_1x512":
         traffic = measured_traffic("gate_up_gemm_mini_f16_1x512_traffic.md", "logits_parity_amd/csrc/gemm.hpp")
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
-            "kernel": "phi_gemm_mfma_kernel<EPI_SILU> (fused gate/up + SiLU*up)",
-            "avg_launch_us": round(avg_s * 1e6, 2), "flops_per_launch": kflops}
+            "kernel": "phi_gemm_mfma_kernel<..., EPI_SILU> (fused gate/up GEMM + SiLU*up)",
+            "avg_launch_us": round(avg_s * 1e6, 2), "flops_per_launch": kflops,
+            "launches_timed": gu_n}
+    stages = {k: round(v[0] / n_prof, 4) for k, v in prof.items()}
 
     out = {"metric": "Phi-3-mini-shape f16 prefill tokens/s, % MFMA peak; logit cosine vs oracle",
            "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -232,6 +231,7 @@ def main():
            "roofline": roof,
            "model_mfma_frac": round(flops / (wall / args.steps) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
            "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),
+           "stage_ms_per_step": stages,
            "logits_finite": finite}
 
     if not args.no_decode:

@@ -139,6 +139,29 @@ void phi_free(phi_model* m);
 /* Static text for a status code. */
 const char* phi_strerror(int32_t status);
 
+/* ---- per-stage device timing of phi_prefill_logits ------------------------
+ * Off by default.  When enabled, every kernel launch of phi_prefill_logits is
+ * bracketed by two HIP events on the call's stream, so a stage's time is the
+ * device time of its own launches inside real forwards.  phi_profile_read
+ * waits for the recorded events, writes per-stage total milliseconds and
+ * launch counts (arrays of PHI_PROF_N), and clears the record.  Events are
+ * created on the first enabled call; at most 16 forwards may be recorded
+ * between reads (PHI_E_RANGE otherwise, checked before anything is enqueued).
+ * Not for concurrent use of one model from several threads. */
+enum {
+  PHI_PROF_EMBED = 0,   /* embedding gather + first RMSNorm */
+  PHI_PROF_QKV = 1,     /* fused QKV GEMM + RoPE */
+  PHI_PROF_ATTN = 2,    /* causal attention */
+  PHI_PROF_O = 3,       /* o_proj GEMM (+ residual or split partials) */
+  PHI_PROF_NORM = 4,    /* RMSNorm (+ split-K reduce) after o_proj and down */
+  PHI_PROF_GATE_UP = 5, /* fused gate/up GEMM + SiLU*up */
+  PHI_PROF_DOWN = 6,    /* down GEMM (+ residual or split partials) */
+  PHI_PROF_LM_HEAD = 7, /* lm_head GEMM */
+  PHI_PROF_N = 8
+};
+phi_status phi_profile_enable(phi_model* m, int32_t enable);
+phi_status phi_profile_read(phi_model* m, double* ms_out, int64_t* launches_out);
+
 /* ---- building blocks, exposed for kernel-level checks ------------------- */
 
 /* y[M][N] (float32) = a[M][K] w[N][K]^T with the prefill GEMM kernel.
@@ -194,6 +217,31 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
                              int32_t n_pages, int32_t max_pages, int32_t max_ctx, float sm_scale, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- K16/V8 cache write ([P3]) --------------------------------------------
+ * The step before decode attention: append one token per sequence to the
+ * paged pool ([P3] names the write of the compressed cache in its
+ * candidate-kernel description).  For sequence b and KV head g, with
+ * t = positions[b], page = block_table[b][t / 16] and slot = t % 16:
+ *   k_pool[page][g][slot][:] = k_new[b][g][:]            (binary16, copied)
+ *   v_pool[page][g][slot][d] = E4M3(v_new[b][g][d] / v_scale[g])
+ * where the quotient is an IEEE fp32 division and E4M3 rounds it to the
+ * nearest OCP E4M3FN value, ties to even, saturating magnitudes above 448 to
+ * +-448 and mapping NaN to 0x7F.  Nothing else in the pools changes.
+ *   k_new, v_new binary16 [B][n_kv_heads][D]
+ *   v_scale  float32 [n_kv_heads]
+ *   block_table int32 [B][max_pages], positions int32 [B] (device)
+ *   k_pool binary16 / v_pool uint8 [n_pages][n_kv_heads][16][D], updated in place
+ * Supported: D = 128, page_size = 16.  batch = 0 returns PHI_OK before any
+ * other check (the per-sequence pointers may then be NULL).  Two
+ * sequences must not name the same (page, slot).  Device-side values are
+ * checked in the kernel: a sequence whose position lies outside
+ * [0, max_pages * 16) or whose page id lies outside [0, n_pages) is not
+ * written. */
+phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,
+                           const int32_t* positions, int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t n_pages, int32_t max_pages, void* k_pool, void* v_pool,
+                           void* stream);
 
 /* Token slots per layer of a KV pool of budget_bytes split evenly over
  * n_layers, each token holding one key of k_bytes and one value of v_bytes per

@@ -16,11 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libphi.so")
 
 PHI_WT_F32, PHI_WT_F16, PHI_WT_I8 = 0, 1, 2
+PROF_STAGES = ("embed", "qkv", "attn", "o_proj", "norm", "gate_up", "down", "lm_head")
+PROF_N = len(PROF_STAGES)
 WTYPES = {"f32": PHI_WT_F32, "f16": PHI_WT_F16, "i8": PHI_WT_I8}
 
 EXPORTS = ("phi_state_bytes", "phi_load_fused", "phi_workspace_bytes", "phi_prefill_logits", "phi_free",
            "phi_strerror", "phi_linear_f32out", "phi_gate_up_silu", "phi_attention_vt_stride", "phi_attention_prefill",
-           "attn_decode_k16v8_workspace_bytes", "attn_decode_k16v8", "phi_kv_pool_slots")
+           "attn_decode_k16v8_workspace_bytes", "attn_decode_k16v8", "phi_kv_pool_slots", "phi_profile_enable",
+           "phi_profile_read", "kv_append_k16v8")
 
 
 class PhiError(RuntimeError):
@@ -75,7 +78,10 @@ def lib() -> ctypes.CDLL:
         "phi_attention_prefill": (i32, [i32, P, P, P, P, i32, i32, i32, i32, i32, P]),
         "attn_decode_k16v8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "attn_decode_k16v8": (i32, [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, sz, P]),
+        "kv_append_k16v8": (i32, [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]),
         "phi_kv_pool_slots": (i64, [i64, i32, i32, i32, i32, i32, i32]),
+        "phi_profile_enable": (i32, [P, i32]),
+        "phi_profile_read": (i32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -142,6 +148,16 @@ class Model:
 
     def prefill_logits(self, ids, logits=None, workspace=None, stream=None):
         return phi_prefill_logits(self, ids, logits, workspace, stream)
+
+    def profile_enable(self, enable: bool = True):
+        _check(lib().phi_profile_enable(self.handle, int(enable)), "phi_profile_enable")
+
+    def profile_read(self) -> dict:
+        """Per-stage device milliseconds and launch counts since the last read."""
+        ms = (ctypes.c_double * PROF_N)()
+        n = (ctypes.c_int64 * PROF_N)()
+        _check(lib().phi_profile_read(self.handle, ms, n), "phi_profile_read")
+        return {name: (ms[i], n[i]) for i, name in enumerate(PROF_STAGES)}
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -234,6 +250,15 @@ def attn_decode_k16v8(q, k_pool, v_pool, v_scale, block_table, ctx_lens, max_ctx
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_decode_k16v8")
     return out
+
+
+def kv_append_k16v8(k_new, v_new, v_scale, block_table, positions, k_pool, v_pool, stream=None):
+    """Append one token per sequence to the K16/V8 pools in place; see include/phi.h."""
+    B, Hkv, D = k_new.shape
+    P, _, page, _ = k_pool.shape
+    _check(lib().kv_append_k16v8(_ptr(k_new), _ptr(v_new), _ptr(v_scale), _ptr(block_table), _ptr(positions), B,
+                                 Hkv, D, page, P, block_table.shape[1], _ptr(k_pool), _ptr(v_pool),
+                                 _stream(stream)), "kv_append_k16v8")
 
 
 def phi_kv_pool_slots(budget_bytes: int, n_layers: int, n_kv_heads: int, head_dim: int, k_bytes: int,

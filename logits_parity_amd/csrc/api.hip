@@ -17,8 +17,17 @@
 
 using namespace phi;
 
+// Event pairs bracketing the launches of recorded forwards.
+struct PhiProfile {
+  bool enabled = false;
+  std::vector<hipEvent_t> ev;  // 2 per launch slot
+  std::vector<int> stage;      // stage of each used slot
+  size_t used = 0;
+};
+
 struct phi_model {
   phi_config cfg;
+  PhiProfile prof;
   std::vector<phi_layer_weights> layers;
   const void* embed;
   const void* final_norm;
@@ -222,9 +231,31 @@ phi_status norm(bool embed, NormArgs a, hipStream_t st) {
   return launched();
 }
 
+// Records the start event of a launch slot when profiling (no-op otherwise).
+struct StageTimer {
+  PhiProfile* p;
+  hipStream_t st;
+  size_t slot = 0;
+  bool on = false;
+  void begin(int stage) {
+    on = p->enabled;
+    if (!on) return;
+    slot = p->used++;
+    p->stage[slot] = stage;
+    (void)hipEventRecord(p->ev[2 * slot], st);
+  }
+  void end() {
+    if (on) (void)hipEventRecord(p->ev[2 * slot + 1], st);
+  }
+};
+
+// Launch slots of one forward: embed + per layer (qkv, attn, o, norm, gate_up, down, norm) + lm_head.
+inline size_t launches_per_forward(const phi_config& c) { return 2 + 7 * (size_t)c.n_layers; }
+
 template <class AT>
 phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, float* logits, char* ws,
                    hipStream_t st) {
+  StageTimer tm{const_cast<PhiProfile*>(&m->prof), st};
   const phi_config& c = m->cfg;
   const PrefillPlan p = plan_prefill(c, batch, seq);
   const int T = p.T, H = c.hidden, I = c.intermediate, hd = c.head_dim;
@@ -246,7 +277,9 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   na.V = c.vocab;
   na.eps = c.rms_eps;
   na.gain = m->layers[0].ln1;
+  tm.begin(PHI_PROF_EMBED);
   phi_status s = norm<AT, AT>(true, na, st);
+  tm.end();
   if (s) return s;
 
   GemmArgs base{};
@@ -280,9 +313,15 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.q = const_cast<void*>(aa.q);
     g.k = const_cast<void*>(aa.k);
     g.vt = const_cast<void*>(aa.vt);
-    if ((s = gemm<EPI_QKV>(wt, g, p.qkv, st))) return s;
+    tm.begin(PHI_PROF_QKV);
+    s = gemm<EPI_QKV>(wt, g, p.qkv, st);
+    tm.end();
+    if (s) return s;
 
-    if ((s = attention(wt == PHI_WT_F32, aa, batch, st))) return s;
+    tm.begin(PHI_PROF_ATTN);
+    s = attention(wt == PHI_WT_F32, aa, batch, st);
+    tm.end();
+    if (s) return s;
 
     g = base;
     g.A = attn;
@@ -293,10 +332,16 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.x = x;
     g.ldx = H;
     g.out = part;
-    if ((s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit))) return s;
+    tm.begin(PHI_PROF_O);
+    s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit);
+    tm.end();
+    if (s) return s;
 
     na.gain = L.ln2;
-    if ((s = norm<AT, AT>(false, na, st))) return s;
+    tm.begin(PHI_PROF_NORM);
+    s = norm<AT, AT>(false, na, st);
+    tm.end();
+    if (s) return s;
 
     g = base;
     g.A = xn;
@@ -306,7 +351,10 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.K = H;
     g.act = act;
     g.ld_act = I;
-    if ((s = gemm<EPI_SILU>(wt, g, p.gu, st))) return s;
+    tm.begin(PHI_PROF_GATE_UP);
+    s = gemm<EPI_SILU>(wt, g, p.gu, st);
+    tm.end();
+    if (s) return s;
 
     g = base;
     g.A = act;
@@ -317,10 +365,16 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.x = x;
     g.ldx = H;
     g.out = part;
-    if ((s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit))) return s;
+    tm.begin(PHI_PROF_DOWN);
+    s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit);
+    tm.end();
+    if (s) return s;
 
     na.gain = l + 1 < c.n_layers ? m->layers[l + 1].ln1 : m->final_norm;
-    if ((s = norm<AT, AT>(false, na, st))) return s;
+    tm.begin(PHI_PROF_NORM);
+    s = norm<AT, AT>(false, na, st);
+    tm.end();
+    if (s) return s;
   }
 
   GemmArgs g = base;
@@ -331,7 +385,10 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   g.K = H;
   g.out = logits;
   g.ldo = c.vocab;
-  return gemm<EPI_F32>(wt, g, p.lm, st);
+  tm.begin(PHI_PROF_LM_HEAD);
+  s = gemm<EPI_F32>(wt, g, p.lm, st);
+  tm.end();
+  return s;
 }
 
 // ---------------------------------------------------------------- decode plan
@@ -449,11 +506,49 @@ phi_status phi_prefill_logits(const phi_model* m, const int32_t* ids, int32_t ba
   if (!aligned16(ids) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
   hipStream_t st = as_stream(stream);
   char* ws = reinterpret_cast<char*>(workspace);
+  const PhiProfile& pr = m->prof;
+  if (pr.enabled && pr.used + launches_per_forward(m->cfg) > pr.stage.size()) return PHI_E_RANGE;
   if (m->cfg.wtype == PHI_WT_F32) return forward<float>(m, ids, batch, seq, logits, ws, st);
   return forward<f16>(m, ids, batch, seq, logits, ws, st);
 }
 
-void phi_free(phi_model* m) { delete m; }
+void phi_free(phi_model* m) {
+  if (!m) return;
+  for (hipEvent_t e : m->prof.ev) (void)hipEventDestroy(e);
+  delete m;
+}
+
+phi_status phi_profile_enable(phi_model* m, int32_t enable) {
+  if (!m) return PHI_E_NULL;
+  PhiProfile& p = m->prof;
+  if (enable && p.ev.empty()) {
+    const size_t slots = 16 * launches_per_forward(m->cfg);
+    p.ev.resize(2 * slots);
+    p.stage.assign(slots, 0);
+    for (hipEvent_t& e : p.ev)
+      if (hipEventCreate(&e) != hipSuccess) return PHI_E_HIP;
+  }
+  p.enabled = enable != 0;
+  return PHI_OK;
+}
+
+phi_status phi_profile_read(phi_model* m, double* ms_out, int64_t* launches_out) {
+  if (!m || !ms_out || !launches_out) return PHI_E_NULL;
+  PhiProfile& p = m->prof;
+  for (int i = 0; i < PHI_PROF_N; ++i) {
+    ms_out[i] = 0.0;
+    launches_out[i] = 0;
+  }
+  if (p.used && hipEventSynchronize(p.ev[2 * p.used - 1]) != hipSuccess) return PHI_E_HIP;
+  for (size_t i = 0; i < p.used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) return PHI_E_HIP;
+    ms_out[p.stage[i]] += ms;
+    launches_out[p.stage[i]] += 1;
+  }
+  p.used = 0;
+  return PHI_OK;
+}
 
 phi_status phi_linear_f32out(int32_t wtype, const void* a, const void* w, const void* scale, float* y, int32_t M,
                              int32_t N, int32_t K, void* stream) {
@@ -566,6 +661,34 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
   }
   if (hipGetLastError() != hipSuccess) return PHI_E_HIP;
   hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
+  return launched();
+}
+
+phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,
+                           const int32_t* positions, int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t n_pages, int32_t max_pages, void* k_pool, void* v_pool,
+                           void* stream) {
+  if (batch == 0) return PHI_OK;
+  if (!k_new || !v_new || !v_scale || !block_table || !positions || !k_pool || !v_pool) return PHI_E_NULL;
+  if (batch < 0 || n_kv_heads < 1 || head_dim != 128 || page_size != 16 || n_pages < 1 || max_pages < 1)
+    return PHI_E_SHAPE;
+  if ((long long)n_pages * n_kv_heads * 16 * 128 * 2 > (1ll << 40) || (long long)batch * n_kv_heads > (1 << 26))
+    return PHI_E_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)) return PHI_E_ALIGN;
+  KvAppendArgs a{};
+  a.k_new = reinterpret_cast<const f16*>(k_new);
+  a.v_new = reinterpret_cast<const f16*>(v_new);
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.positions = positions;
+  a.k_pool = reinterpret_cast<f16*>(k_pool);
+  a.v_pool = reinterpret_cast<uint8_t*>(v_pool);
+  a.B = batch;
+  a.Hkv = n_kv_heads;
+  a.n_pages = n_pages;
+  a.max_pages = max_pages;
+  const int rows = batch * n_kv_heads;
+  hipLaunchKernelGGL(phi_kv_append_kernel, dim3((rows + 15) / 16), dim3(256), 0, as_stream(stream), a);
   return launched();
 }
 

@@ -239,3 +239,68 @@ __global__ __launch_bounds__(128) void phi_decode_merge_kernel(DecodeArgs a) {
 }
 
 }  // namespace phi
+
+namespace phi {
+
+// ---- K16/V8 cache write ----------------------------------------------------
+// One decode step appends one token per sequence: its binary16 key goes into
+// the page slot as is, its value becomes the E4M3 code of the fp32 quotient
+// v / v_scale[g], rounded to nearest-even and saturated to +-448 (NaN keeps a
+// NaN code).  A group of 16 lanes owns one (sequence, KV head) row; lane j
+// moves dims 8 j .. 8 j + 7: a 16-byte key store and an 8-byte value store.
+
+struct KvAppendArgs {
+  const f16* k_new;   // [B][Hkv][128]
+  const f16* v_new;   // [B][Hkv][128]
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* positions;
+  f16* k_pool;        // [n_pages][Hkv][16][128]
+  uint8_t* v_pool;    // [n_pages][Hkv][16][128]
+  int B, Hkv, n_pages, max_pages;
+};
+
+// Quotient ready for the hardware conversion: clamped into [-448, 448] so the
+// conversion saturates instead of overflowing; NaN passes through.
+__device__ __forceinline__ float e4m3_operand(float v, float s) {
+  const float x = v / s;
+  return x != x ? x : fminf(fmaxf(x, -448.f), 448.f);
+}
+
+// Four values to four E4M3 bytes (byte i = value i), NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  uint32_t u = static_cast<uint32_t>(w);
+  const float x[4] = {x0, x1, x2, x3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (x[i] != x[i]) u = (u & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i));
+  return u;
+}
+
+__global__ __launch_bounds__(256) void phi_kv_append_kernel(KvAppendArgs a) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (row >= a.B * a.Hkv) return;
+  const int b = row / a.Hkv, g = row - b * a.Hkv;
+  const int t = a.positions[b];
+  if (t < 0 || t >= a.max_pages * 16) return;
+  const int page = a.block_table[(size_t)b * a.max_pages + (t >> 4)];
+  if (page < 0 || page >= a.n_pages) return;
+  const size_t src = (size_t)row * 128 + j * 8;
+  const size_t dst = (((size_t)page * a.Hkv + g) * 16 + (t & 15)) * 128 + j * 8;
+  *reinterpret_cast<uint4*>(a.k_pool + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
+  const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
+  const f16* vh = reinterpret_cast<const f16*>(&vv);
+  const float s = a.v_scale[g];
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = e4m3_operand(static_cast<float>(vh[i]), s);
+  uint2 out;
+  out.x = e4m3_pack4(x[0], x[1], x[2], x[3]);
+  out.y = e4m3_pack4(x[4], x[5], x[6], x[7]);
+  *reinterpret_cast<uint2*>(a.v_pool + dst) = out;
+}
+
+}  // namespace phi

@@ -108,6 +108,18 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.attn_decode_k16v8_workspace_bytes(32, 40, 10, 128, 1024) > 0
     assert L.attn_decode_k16v8_workspace_bytes(32, 40, 10, 96, 1024) == 0
 
+    def app(**kw):
+        p = dict(batch=2, hkv=2, d=128, page=16, n_pages=8, max_pages=4, k_new=0x100, k_pool=0x600)
+        p.update(kw)
+        return L.kv_append_k16v8(p["k_new"], 0x200, 0x300, 0x400, 0x500, p["batch"], p["hkv"], p["d"], p["page"],
+                                 p["n_pages"], p["max_pages"], p["k_pool"], 0x700, None)
+    assert app(k_new=None) == 1
+    assert app(d=96) == 2
+    assert app(page=8) == 2
+    assert app(batch=-1) == 2
+    assert app(k_pool=0x604) == 6
+    assert app(batch=0) == 0               # nothing to write, nothing enqueued
+
 
 def test_no_packed_fp32_instructions_in_device_code(tmp_path):
     """Device code is built with packed fp32 math disabled; check the ISA of
