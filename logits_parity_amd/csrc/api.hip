@@ -208,19 +208,7 @@ phi_status attention(bool f32, AttnArgs a, int batch, hipStream_t st) {
     hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
     return launched();
   }
-  // more queries per workgroup when there are enough workgroups to fill the
-  // chip; otherwise 32 queries per workgroup with the keys split over 4 waves
-  const long units = (long)batch * a.nh;
-  if (units * ((a.S + 127) / 128) < 512) {
-    hipLaunchKernelGGL(phi_attn_prefill_split_kernel<4>, dim3((a.S + 31) / 32, a.nh, batch), dim3(256), 0, st, a);
-    return launched();
-  }
-  if (units * ((a.S + 127) / 128) >= 512)
-    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<4>, dim3((a.S + 127) / 128, a.nh, batch), dim3(256), 0, st, a);
-  else if (units * ((a.S + 63) / 64) >= 256)
-    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<2>, dim3((a.S + 63) / 64, a.nh, batch), dim3(128), 0, st, a);
-  else
-    hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<1>, dim3((a.S + 31) / 32, a.nh, batch), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<4>, dim3((a.S + 31) / 32, a.nh, batch), dim3(256), 0, st, a);
   return launched();
 }
 
