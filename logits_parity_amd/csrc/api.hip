@@ -95,11 +95,22 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8) {
   return p;
 }
 
+// LDS stages of a tile.  Tiles whose two stages leave room for a second
+// workgroup per CU keep 2 (the other workgroup covers the load latency);
+// larger tiles take 3 when they fit in 152 KB.  int8 weights, which stage
+// through VGPRs one k-step ahead, use 2.
+template <class C, bool W8>
+constexpr int gemm_stages() {
+  constexpr int stage_bytes = (C::BM + C::BN) * 64 * 2;
+  if (W8 || 2 * stage_bytes <= 64 * 1024) return 2;
+  return 3 * stage_bytes <= 152 * 1024 ? 3 : 2;
+}
+
 template <class C, bool W8, int EPI>
 void launch_mfma(GemmArgs a, hipStream_t st) {
   const int units = a.tiles_m * a.tiles_n * a.splits;
   const int grid = (units + 7) / 8 * 8;
-  hipLaunchKernelGGL((phi_gemm_mfma_kernel<C, W8, EPI>), dim3(grid), dim3(C::NT), 0, st, a);
+  hipLaunchKernelGGL((phi_gemm_mfma_kernel<C, W8, EPI, gemm_stages<C, W8>()>), dim3(grid), dim3(C::NT), 0, st, a);
 }
 
 template <bool W8, int EPI>

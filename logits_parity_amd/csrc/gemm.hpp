@@ -3,12 +3,14 @@
 // MFMA core (binary16 activations; binary16 or int8 weights):
 //  - 4 waves of 64 lanes, each owning a WM x WN sub-tile built from
 //    v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators.
-//  - K is walked in steps of 64 through two LDS stages.  binary16 operands go
-//    global -> LDS directly (global_load_lds_dwordx4, no VGPR staging): one
-//    wave instruction fills 1 KB = 8 rows of 128 B.  int8 weights are loaded
-//    into VGPRs, widened exactly to binary16 (|q| <= 127) and written to LDS;
-//    their per-row scale multiplies the fp32 accumulator (it factors out of
-//    the K sum).
+//  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
+//    them in flight while one is consumed, so the DMA of a k-step has NS - 1
+//    k-steps of MFMA work to arrive.  binary16 operands go global -> LDS
+//    directly (global_load_lds_dwordx4, no VGPR staging): one wave
+//    instruction fills 1 KB = 8 rows of 128 B.  int8 weights are loaded
+//    into VGPRs, widened exactly to binary16 (|q| <= 127) and written to LDS
+//    one k-step ahead (NS = 2); their per-row scale multiplies the fp32
+//    accumulator (it factors out of the K sum).
 //  - Rows are stored with an XOR swizzle of their 16-byte chunks,
 //    chunk' = chunk ^ ((row >> 1) & 7): 16 lanes reading 16 consecutive rows
 //    at one logical chunk touch 16 distinct 16-byte bank groups of the
@@ -33,8 +35,9 @@
 //               are read in the order d = 0..31 | 48..79 | 32..47, 80..95 so
 //               that RoPE pairs (d, d + 48) sit in one lane (first two blocks)
 //               or in lanes l and l ^ 16 (third block).  RoPE runs on the fp32
-//               accumulator; Q, K go to [B][heads][S][96], V to
-//               V^T [B][kv_heads][96][s_pad].
+//               accumulator; the head tile is staged through LDS in natural
+//               d order and written with 16-byte stores: Q, K to
+//               [B][heads][S][96], V to V^T [B][kv_heads][96][s_pad].
 // fp32 core (float32 model): a SIMT kernel with an LDS-staged epilogue.
 #pragma once
 #include "common.hpp"
@@ -91,6 +94,12 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 // s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
 #define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only.  __syncthreads() would also wait for every outstanding global load,
+// draining the DMA stages that are meant to stay in flight; the DMA stage a
+// k-step reads is waited for explicitly (vmcnt) before this barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
@@ -112,10 +121,11 @@ struct TileCfg {
   static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
 };
 
-template <class C, bool W8, int EPI>
+template <class C, bool W8, int EPI, int NS>
 __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
   constexpr int NT = C::NT, NW = C::NW, BK = 64;
+  static_assert(NS >= 2 && NS <= 4 && (!W8 || NS == 2), "stages: int8 weights stage through VGPRs, 2 stages");
   constexpr int STAGE = (BM + BN) * BK;              // f16 elements per LDS stage
   constexpr int INS_A = BM * 8 / 64;                 // 1 KB DMA instructions for A per stage
   constexpr int INS_W = W8 ? 0 : BN * 8 / 64;
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   static_assert(EPI != EPI_QKV || WN == 96, "QKV: one head per wave");
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
 
-  __shared__ __attribute__((aligned(1024))) f16 smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) f16 smem[NS * STAGE];
 
   const int n_units = a.tiles_m * a.tiles_n * a.splits;
   const int unit = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -197,26 +207,36 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 
   const int kt0 = split * a.kt_per_split;
   const int kt1 = min(K / BK, kt0 + a.kt_per_split);
-  if (kt0 < kt1) {
-    issue(kt0, smem);
-    if constexpr (W8) store_w8(smem);
+  // stages kt0 .. kt0 + NS - 2 in flight before the first k-step
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
+  if constexpr (W8) {
+    if (kt0 < kt1) store_w8(smem);
   }
   for (int kt = kt0; kt < kt1; ++kt) {
-    f16* cur = smem + ((kt - kt0) & 1) * STAGE;
-    f16* nxt = smem + ((kt - kt0 + 1) & 1) * STAGE;
-    PHI_WAIT_VMCNT(0);
-    __syncthreads();
-    const bool more = kt + 1 < kt1;
-    if (more) issue(kt + 1, nxt);
+    const int rel = kt - kt0;
+    f16* cur = smem + (rel % NS) * STAGE;
+    f16* nxt = smem + ((rel + NS - 1) % NS) * STAGE;  // the stage read in step kt - 1
+    // wait for this wave's DMA of stage kt; the newer stages stay in flight
+    const int newer = min(NS - 2, kt1 - 1 - kt);
+    if (newer <= 0) PHI_WAIT_VMCNT(0);
+    else if (newer == 1) PHI_WAIT_VMCNT(LPW);
+    else PHI_WAIT_VMCNT(2 * LPW);
+    lds_barrier();
+    const bool more = kt + NS - 1 < kt1;
+    if (more) issue(kt + NS - 1, nxt);
     f16x8 af[2][TM], bf[2][TN];
+    // B fragments first, then A in MFMA order: the first MFMAs of a step
+    // wait only for the oldest reads, the last reads overlap with them
     auto ld = [&](int kk, f16x8* fa, f16x8* fb) {
       const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + i * 32 + (lane & 31), c));
-#pragma unroll
       for (int j = 0; j < TN; ++j)
         fb[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(wn * WN + j * 32 + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + i * 32 + (lane & 31), c));
     };
     ld(0, af[0], bf[0]);
 #pragma unroll
@@ -292,37 +312,95 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
         }
     }
   } else {  // EPI_QKV
-    const int col0 = tn * BN + wn * 96;  // first fused row of this wave's head
-    if (col0 >= a.N) return;
+    // RoPE on the accumulators, then the wave's WM x 96 head tile goes through
+    // LDS in natural d order and leaves as 16-byte stores: rows of Q / K, and
+    // rows of V^T (64 tokens = 128 B per row segment).
+    constexpr int QLD = 104;              // Q/K staging row stride (conflict-free writes)
+    constexpr int VLD = WM + 8;           // V^T staging row stride
+    constexpr int REG = (WM * QLD > 96 * VLD) ? WM * QLD : 96 * VLD;
+    static_assert(NW * REG <= NS * STAGE, "QKV staging fits in the stage buffers");
+    const int col0 = tn * BN + wn * 96;   // first fused row of this wave's head
     const int q_end = a.nh * 96, k_end = (a.nh + a.nkv) * 96;
     const bool is_v = col0 >= k_end;
     const int head = col0 < q_end ? col0 / 96 : (col0 < k_end ? (col0 - q_end) / 96 : (col0 - k_end) / 96);
     const int nheads = col0 < q_end ? a.nh : a.nkv;
-    f16* dst = reinterpret_cast<f16*>(col0 < q_end ? a.q : a.k);
-    f16* vt = reinterpret_cast<f16*>(a.vt);
     const int d0 = col_l, d1 = 48 + col_l, d2 = col_l < 16 ? 32 + col_l : 64 + col_l;
     const int f2 = 32 + (col_l & 15);  // frequency index of the third block's pair
+    const int mw0 = m0 + wm * WM;      // first token row of this wave
+    // rotation factors of the lane's rows: all loads in flight at once, before
+    // the barrier (position s = token row mod S, from one division per lane)
+    float c0[TM][16], s0[TM][16], c2[TM][16], s2[TM][16];
+    if (!is_v && col0 < a.N) {
+      const int s_base = mw0 - (mw0 / a.S) * a.S;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = row_of(i, v);
-        const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1], y2 = acc[i][2][v] * sc[2];
-        const float y2p = __shfl_xor(y2, 16);  // partner of the third block (all lanes take part)
+        for (int v = 0; v < 16; ++v) {
+          int sp = s_base + i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+          while (sp >= a.S) sp -= a.S;
+          const size_t t = (size_t)sp * 48;
+          c0[i][v] = a.rope_cos[t + col_l];
+          s0[i][v] = a.rope_sin[t + col_l];
+          c2[i][v] = a.rope_cos[t + f2];
+          s2[i][v] = a.rope_sin[t + f2];
+        }
+    }
+    __syncthreads();                      // every wave is done with the k-stages
+    if (col0 >= a.N) return;
+    f16* tile = smem + wave * REG;
+    if (is_v) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+          tile[d0 * VLD + r] = (f16)(acc[i][0][v] * sc[0]);
+          tile[d1 * VLD + r] = (f16)(acc[i][1][v] * sc[1]);
+          tile[d2 * VLD + r] = (f16)(acc[i][2][v] * sc[2]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+          const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1], y2 = acc[i][2][v] * sc[2];
+          const float y2p = __shfl_xor(y2, 16);  // partner of the third block
+          tile[r * QLD + d0] = (f16)(y0 * c0[i][v] - y1 * s0[i][v]);
+          tile[r * QLD + d1] = (f16)(y1 * c0[i][v] + y0 * s0[i][v]);
+          tile[r * QLD + d2] = (f16)(col_l < 16 ? y2 * c2[i][v] - y2p * s2[i][v] : y2 * c2[i][v] + y2p * s2[i][v]);
+        }
+    }
+    // the wave reads back only what it wrote: its own LDS operations are ordered
+    if (!is_v) {
+      f16* dst = reinterpret_cast<f16*>(col0 < q_end ? a.q : a.k);
+      for (int idx = lane; idx < WM * 12; idx += 64) {
+        const int r = idx / 12, c = idx - r * 12;
+        const int m = mw0 + r;
         if (m >= a.M) continue;
         const int b = m / a.S, s = m - b * a.S;
-        if (is_v) {
-          f16* base = vt + ((size_t)(b * a.nkv + head) * 96) * a.s_pad + s;
-          base[(size_t)d0 * a.s_pad] = (f16)y0;
-          base[(size_t)d1 * a.s_pad] = (f16)y1;
-          base[(size_t)d2 * a.s_pad] = (f16)y2;
+        *reinterpret_cast<f16x8*>(dst + ((size_t)(b * nheads + head) * a.S + s) * 96 + c * 8) =
+            *reinterpret_cast<const f16x8*>(tile + r * QLD + c * 8);
+      }
+    } else {
+      f16* vt = reinterpret_cast<f16*>(a.vt);
+      constexpr int CPR = WM / 8;  // 8-token chunks per V^T row segment
+      const bool aligned = (a.S & 7) == 0;  // then a chunk never straddles two sequences
+      for (int idx = lane; idx < 96 * CPR; idx += 64) {
+        const int d = idx / CPR, c = idx - d * CPR;
+        const int m = mw0 + c * 8;
+        if (m >= a.M) continue;
+        if (aligned) {
+          const int b = m / a.S, s = m - b * a.S;
+          *reinterpret_cast<f16x8*>(vt + ((size_t)(b * a.nkv + head) * 96 + d) * a.s_pad + s) =
+              *reinterpret_cast<const f16x8*>(tile + d * VLD + c * 8);
         } else {
-          const float c0 = a.rope_cos[(size_t)s * 48 + col_l], s0 = a.rope_sin[(size_t)s * 48 + col_l];
-          const float c2 = a.rope_cos[(size_t)s * 48 + f2], s2 = a.rope_sin[(size_t)s * 48 + f2];
-          f16* base = dst + ((size_t)(b * nheads + head) * a.S + s) * 96;
-          base[d0] = (f16)(y0 * c0 - y1 * s0);
-          base[d1] = (f16)(y1 * c0 + y0 * s0);
-          base[d2] = (f16)(col_l < 16 ? y2 * c2 - y2p * s2 : y2 * c2 + y2p * s2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (m + e >= a.M) break;
+            const int b = (m + e) / a.S, s = m + e - b * a.S;
+            vt[((size_t)(b * a.nkv + head) * 96 + d) * a.s_pad + s] = tile[d * VLD + c * 8 + e];
+          }
         }
       }
     }
