@@ -176,6 +176,13 @@ TINY = PhiConfig("tiny", n_layers=2, hidden=384, n_heads=4, n_kv_heads=4, head_d
 MINI = PhiConfig("mini", n_layers=32, hidden=3072, n_heads=32, n_kv_heads=32, head_dim=96,
                  intermediate=8192, vocab=32064, wtype="f16")
 MINI_W8 = replace(MINI, name="mini_w8", wtype="i8")
+# grouped-query attention at head_dim 128 (the Phi-4 geometry): a small model
+# for oracle pins and one layer at full Phi-4 width (hidden 5120, 40 query
+# heads over 10 KV heads, intermediate 17920, RoPE base 250000)
+TINY_GQA128 = PhiConfig("tiny_gqa128", n_layers=2, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128,
+                        intermediate=1024, vocab=4096, rope_theta=250000.0, wtype="f16")
+PHI4_1L = PhiConfig("phi4_1l", n_layers=1, hidden=5120, n_heads=40, n_kv_heads=10, head_dim=128,
+                    intermediate=17920, vocab=100352, rope_theta=250000.0, wtype="f16")
 
 
 @dataclass(frozen=True)

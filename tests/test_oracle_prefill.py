@@ -91,6 +91,16 @@ def test_matches_transformers_gqa_gain_one_peaked():
     _hf_pin(cfg, ws, ids, 1e-4)
 
 
+def test_matches_transformers_head_dim_128_gqa_peaked():
+    # the Phi-4 head geometry: head_dim 128, four query heads per KV head,
+    # RoPE base 250000, unit gains and peaked attention
+    cfg = replace(synth.TINY_GQA128, norm_gain="ones")
+    ws = ScaledWeights(synth.WeightSet(cfg), 2.5)
+    ids = synth.token_ids(cfg, 2, 24)
+    ours, ref = _hf_pin(cfg, ws, ids, 1e-4)
+    assert np.abs(ref).max() > 1.0   # the regime is not dominated by the embedding
+
+
 def _mutants():
     good_rope, good_attn = prefill.apply_rope, prefill.causal_attention
 
