@@ -218,7 +218,8 @@ def phi_attention_vt_stride(seq: int) -> int:
 
 
 def phi_attention_prefill(q, k, vt, out=None, stream=None):
-    """q [B, Hq, S, 96], k [B, Hkv, S, 96], vt [B, Hkv, 96, s_pad] -> out [B, S, Hq * 96]."""
+    """q [B, Hq, S, D], k [B, Hkv, S, D], vt [B, Hkv, D, s_pad] -> out [B, S, Hq * D]; D = 96, or 128
+    for binary16."""
     import torch
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]

@@ -53,7 +53,8 @@ using CfgM = TileCfg<256, 128, 2, 2>;   // wave tile 128 x 64
 using CfgS = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64
 using CfgQL = TileCfg<256, 192, 2, 2>;  // wave tile 128 x 96 (one head per wave)
 using CfgQS = TileCfg<128, 192, 2, 2>;  // wave tile 64 x 96
-enum CfgId { C_L, C_M, C_S, C_QL, C_QS };
+using CfgQ128 = TileCfg<128, 256, 2, 2>;  // wave tile 64 x 128 (one 128-wide head per wave)
+enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128 };
 
 struct GemmPlan {
   int cfg, tiles_m, tiles_n, splits, kpt;
@@ -67,6 +68,7 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
     case C_M: bm = 256; bn = 128; break;
     case C_S: bm = 128; bn = 128; break;
     case C_QL: bm = 256; bn = 192; break;
+    case C_Q128: bm = 128; bn = 256; break;
     default: bm = 128; bn = 192; break;
   }
 }
@@ -76,9 +78,9 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 // for 256 CUs, so K is split until every CU has work.
 // int8 weights stage through VGPRs, which the 256 x 256 tile cannot afford
 // next to its 256 accumulators, so they take the 256 x 128 tile instead.
-GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8) {
+GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   GemmPlan p{};
-  if (epi == EPI_QKV) p.cfg = M >= 1024 ? C_QL : C_QS;
+  if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (M >= 1024 ? C_QL : C_QS);
   else if (epi == EPI_SILU) p.cfg = (M >= 1024 && !w8) ? C_L : C_M;
   else if (epi == EPI_F32) p.cfg = w8 ? C_M : C_L;
   else p.cfg = M >= 2048 ? C_M : C_S;
@@ -117,6 +119,7 @@ template <bool W8, int EPI>
 void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
   if constexpr (EPI == EPI_QKV) {
     if (cfg == C_QL) launch_mfma<CfgQL, W8, EPI>(a, st);
+    else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st);
     else launch_mfma<CfgQS, W8, EPI>(a, st);
   } else if constexpr (EPI == EPI_SILU) {
     if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
@@ -146,7 +149,7 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.s_pad = (int)round_up((size_t)seq, 64);
   const int H = c.hidden, hd = c.head_dim, I = c.intermediate;
   const bool w8 = c.wtype == PHI_WT_I8;
-  p.qkv = plan_gemm(EPI_QKV, p.T, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8);
+  p.qkv = plan_gemm(EPI_QKV, p.T, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8, hd);
   p.o = plan_gemm(EPI_RESID, p.T, H, c.n_heads * hd, w8);
   p.gu = plan_gemm(EPI_SILU, p.T, 2 * I, H, w8);
   p.down = plan_gemm(EPI_RESID, p.T, H, I, w8);
@@ -167,11 +170,13 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   return p;
 }
 
+// head_dim 128 runs on the MFMA paths only (binary16 and int8 weights).
 bool check_config(const phi_config* c) {
-  return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && c->head_dim == 96 &&
+  const bool hd_ok = c->head_dim == 96 || (c->head_dim == 128 && c->wtype != PHI_WT_F32);
+  return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && hd_ok &&
          c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
          (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 128 && c->intermediate % 128 == 0 &&
-         c->hidden <= 4 * 4 * kNormThreads && c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 &&
+         c->hidden <= kNormMaxChunks * 4 * kNormThreads && c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 &&
          c->max_pos <= kMaxPos;
 }
 
@@ -213,13 +218,15 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
   return launched();
 }
 
-phi_status attention(bool f32, AttnArgs a, int batch, hipStream_t st) {
-  a.scale_log2 = kLog2e / sqrtf(96.0f);
+phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
+  a.scale_log2 = kLog2e / sqrtf((float)hd);
   if (f32) {
     hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
     return launched();
   }
-  hipLaunchKernelGGL(phi_attn_prefill_f16_kernel<4>, dim3((a.S + 31) / 32, a.nh, batch), dim3(256), 0, st, a);
+  const dim3 grid((a.S + 31) / 32, a.nh, batch);
+  if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<128, 4>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<96, 4>), grid, dim3(256), 0, st, a);
   return launched();
 }
 
@@ -290,6 +297,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   base.hd = hd;
   base.rope_cos = m->rope_cos;
   base.rope_sin = m->rope_sin;
+  base.max_pos = c.max_pos;
 
   AttnArgs aa{};
   aa.q = ws + p.off_q;
@@ -318,7 +326,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     if (s) return s;
 
     tm.begin(PHI_PROF_ATTN);
-    s = attention(wt == PHI_WT_F32, aa, batch, st);
+    s = attention(wt == PHI_WT_F32, aa, batch, hd, st);
     tm.end();
     if (s) return s;
 
@@ -593,7 +601,8 @@ phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, 
                                  int32_t batch, int32_t seq, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                                  void* stream) {
   if (!q || !k || !vt || !out) return PHI_E_NULL;
-  if (batch < 1 || seq < 1 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads || head_dim != 96)
+  if (batch < 1 || seq < 1 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads ||
+      (head_dim != 96 && !(head_dim == 128 && !act_f32)))
     return PHI_E_SHAPE;
   if (seq > kMaxPos) return PHI_E_RANGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out)) return PHI_E_ALIGN;
@@ -606,7 +615,7 @@ phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, 
   a.s_pad = (int)round_up((size_t)seq, 64);
   a.nh = n_heads;
   a.nkv = n_kv_heads;
-  return attention(act_f32 != 0, a, batch, as_stream(stream));
+  return attention(act_f32 != 0, a, batch, head_dim, as_stream(stream));
 }
 
 size_t attn_decode_k16v8_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

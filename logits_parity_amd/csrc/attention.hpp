@@ -1,4 +1,5 @@
-// Causal softmax attention for the prefill, head_dim 96.
+// Causal softmax attention for the prefill, head_dim 96 (binary16 and float32)
+// or 128 (binary16).
 //
 // binary16 path (split keys, MFMA): a workgroup owns 32 queries of one
 // (sequence, head) and its 4 waves take the 64-key blocks that reach those
@@ -12,7 +13,8 @@
 // each lane holds one query's column: the running max, sum and output rescale
 // are per-lane scalars, and only the max needs one exchange (lanes l, l + 32).
 // The output is accumulated transposed too, O^T += V^T P^T, with P^T taken
-// straight from the score registers.  Key rows enter the score MFMA with bits
+// straight from the score registers.  A key block is 64 keys at head_dim 96
+// and 32 at head_dim 128 (register budget).  Key rows enter the score MFMA with bits
 // 2 and 3 of their index swapped; then the 8 score registers of each half of
 // a lane hold 8 consecutive keys, and the matching V^T operand of the output
 // MFMA is one 16-byte load.  Operands come from bounds-checked buffer loads
@@ -28,12 +30,12 @@
 namespace phi {
 
 struct AttnArgs {
-  const void* q;   // [B][nh][S][96]
-  const void* k;   // [B][nkv][S][96]
-  const void* vt;  // [B][nkv][96][s_pad]
-  void* out;       // [B][S][nh * 96]
+  const void* q;   // [B][nh][S][D]
+  const void* k;   // [B][nkv][S][D]
+  const void* vt;  // [B][nkv][D][s_pad]
+  void* out;       // [B][S][nh * D]
   int S, s_pad, nh, nkv;
-  float scale_log2;  // log2(e) / sqrt(96)
+  float scale_log2;  // log2(e) / sqrt(D)
 };
 
 // Buffer resource over [base, base + bytes): loads outside read as zero.
@@ -41,9 +43,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-template <int NKV>
+template <int D, int NKV>
 __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnArgs a) {
-  constexpr int D = 96, KB = 64, OLD = 100;
+  static_assert(D == 96 || D == 128, "head_dim");
+  constexpr int HB = D == 96 ? 2 : 1;       // 32-key halves per key block (register budget)
+  constexpr int KB = 32 * HB, OLD = D + 4, KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) float sO[NKV][32 * OLD];  // per wave: O[query][d], unnormalised
   __shared__ float sM[NKV][32], sL[NKV][32];
 
@@ -67,26 +71,26 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
   const int koff = (kr * D + grp * 8) * 2;
   const int voff = (col * a.s_pad + 8 * grp) * 2;
 
-  f16x8 qf[6];
+  f16x8 qf[KS];
   {
     const f16* qrow = Q + (size_t)min(qi, S - 1) * D;
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) qf[ks] = *reinterpret_cast<const f16x8*>(qrow + (ks * 2 + grp) * 8);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const f16x8*>(qrow + (ks * 2 + grp) * 8);
   }
-  // operands of one 64-key block, as two 32-key halves
-  f16x8 kf[2][6];
-  f16x8 vf[2][3][2];
+  // operands of one key block, as HB 32-key halves
+  f16x8 kf[HB][KS];
+  f16x8 vf[HB][DB][2];
   auto load = [&](int key0) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       const int k32 = key0 + 32 * hb;
       // the block start goes into the per-lane offset, which the range check covers
       const int kv = koff + k32 * D * 2, vv = voff + k32 * 2;
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
         kf[hb][ks] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, kv + ks * 32, 0, 0));
 #pragma unroll
-      for (int db = 0; db < 3; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv)
           vf[hb][db][hv] = __builtin_bit_cast(
@@ -94,27 +98,27 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
     }
   };
 
-  f32x16 o[3];
+  f32x16 o[DB];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) o[i] = f32x16{};
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   for (int j = 0; j < nj; ++j) {
     const int key0 = (w + NKV * j) * KB;
     load(key0);
-    __builtin_amdgcn_sched_barrier(0);  // all 24 loads of the block in flight before the first MFMA
-    f32x16 sc[2];
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the block in flight before the first MFMA
+    f32x16 sc[HB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       sc[hb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hb][ks], qf[ks], sc[hb], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hb][ks], qf[ks], sc[hb], 0, 0, 0);
     }
     // score register v of half hb holds key key0 + 32 hb + 16 (v / 8) + 8 grp + v % 8
     const bool diag = key0 + KB - 1 > q0;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + 32 * hb + 16 * (v >> 3) + 8 * grp + (v & 7);
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
     const float alpha = exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float e = exp2f(sc[hb][v] - m_new);
@@ -138,12 +142,12 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
     m_run = m_new;
     l_run = l_run * alpha + psum;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) o[i] *= alpha;
+    for (int i = 0; i < DB; ++i) o[i] *= alpha;
     if (key0 + KB > S) {  // value columns >= S are padding: zero them
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int db = 0; db < 3; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
@@ -151,21 +155,21 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
               if (key0 + 32 * hb + 16 * hv + 8 * grp + e >= S) vf[hb][db][hv][e] = (f16)0.f;
     }
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int hv = 0; hv < 2; ++hv) {
         f16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (f16)sc[hb][8 * hv + e];
 #pragma unroll
-        for (int db = 0; db < 3; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[hb][db][hv], pf, o[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[hb][db][hv], pf, o[db], 0, 0, 0);
       }
   }
 
   // this wave's partial state -> LDS (query = col; d rows of O^T)
   const float l_w = l_run + __shfl_xor(l_run, 32);
 #pragma unroll
-  for (int db = 0; db < 3; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) sO[w][col * OLD + db * 32 + 8 * (v >> 2) + 4 * grp + (v & 3)] = o[db][v];
   if (grp == 0) {
@@ -176,8 +180,9 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
   // merge: one (query, 8-dim chunk) per thread and pass, one 16-byte store
   f16* out = reinterpret_cast<f16*>(a.out);
   const int ld = a.nh * D;
-  for (int it = threadIdx.x; it < 32 * 12; it += NKV * 64) {
-    const int qq = it / 12, c = it - qq * 12;
+  constexpr int CH = D / 8;
+  for (int it = threadIdx.x; it < 32 * CH; it += NKV * 64) {
+    const int qq = it / CH, c = it - qq * CH;
     if (q0 + qq >= S) continue;
     float mx = -__builtin_inff();
 #pragma unroll

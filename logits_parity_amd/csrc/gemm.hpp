@@ -31,10 +31,13 @@
 //  EPI_SILU     fused gate/up: the tile reads weight rows in 32-row blocks
 //               alternating gate, up for the same outputs, so a lane holds
 //               gate and up of one output: act = silu(gate) * up
-//  EPI_QKV      fused Q/K/V, one 96-wide head per wave: the head's weight rows
-//               are read in the order d = 0..31 | 48..79 | 32..47, 80..95 so
-//               that RoPE pairs (d, d + 48) sit in one lane (first two blocks)
-//               or in lanes l and l ^ 16 (third block).  RoPE runs on the fp32
+//  EPI_QKV      fused Q/K/V, one head (96 or 128 wide) per wave: the head's
+//               weight rows are read in an order that puts RoPE pairs
+//               (d, d + HD / 2) in one lane (HD = 128: blocks 0..31 | 64..95 |
+//               32..63 | 96..127) or, for the third block of HD = 96 (rows
+//               0..31 | 48..79 | 32..47, 80..95), in lanes l and l ^ 16.  The
+//               RoPE position is the row's index within its sequence, or a
+//               per-row position (decode steps).  RoPE runs on the fp32
 //               accumulator; the head tile is staged through LDS in natural
 //               d order and written with 16-byte stores: Q, K to
 //               [B][heads][S][96], V to V^T [B][kv_heads][96][s_pad].
@@ -63,12 +66,26 @@ struct GemmArgs {
   void* vt;
   const float* rope_cos;  // [max_pos][hd/2]
   const float* rope_sin;
+  const int32_t* pos;     // EPI_QKV: RoPE position of each token row (nullptr: row mod S)
+  int max_pos;
   int S, s_pad, nh, nkv, hd;
 };
 
 // ---------------------------------------------------------------- row maps
-// Weight row read by tile-local row r of N-tile tn (MFMA core).
-template <int EPI, int BN>
+// Position of fused row j (< HD) inside its head for the QKV tiles: RoPE
+// partners (d, d + HD / 2) land in one lane of two 32-row blocks.
+//   HD = 96:  blocks hold d = 0..31 | 48..79 | 32..47, 80..95 (the third
+//             block's partners sit in lanes l and l ^ 16)
+//   HD = 128: blocks hold d = 0..31 | 64..95 | 32..63 | 96..127
+template <int HD>
+__device__ __forceinline__ int qkv_head_row(int j) {
+  if constexpr (HD == 96) return j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
+  else return j < 32 ? j : (j < 64 ? j + 32 : (j < 96 ? j - 32 : j));
+}
+
+// Weight row read by tile-local row r of N-tile tn (MFMA core).  HD: the QKV
+// head width (the wave tile width of QKV tiles).
+template <int EPI, int BN, int HD = 96>
 __device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
   if constexpr (EPI == EPI_SILU) {
     // 32-row blocks alternate gate / up; block pair p covers outputs tn*BN/2 + 32p ..
@@ -76,10 +93,7 @@ __device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
     const int out = tn * (BN / 2) + p * 32 + (r & 31);
     return (blk & 1) ? (a.N >> 1) + out : out;
   } else if constexpr (EPI == EPI_QKV) {
-    const int head_base = tn * BN + (r / 96) * 96;
-    const int j = r % 96;
-    const int d = j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
-    const int n = head_base + d;
+    const int n = tn * BN + (r / HD) * HD + qkv_head_row<HD>(r % HD);
     return n < a.N ? n : a.N - 1;
   } else {
     const int n = tn * BN + r;
@@ -134,7 +148,8 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   static_assert(LPW * NW == INS_A + INS_W, "stage split");
   static_assert(!W8 || CB8 * NT == BN * 4, "int8 split");
   static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
-  static_assert(EPI != EPI_QKV || WN == 96, "QKV: one head per wave");
+  static_assert(EPI != EPI_QKV || WN == 96 || WN == 128, "QKV: one head (96 or 128 wide) per wave");
+  constexpr int HD = EPI == EPI_QKV ? WN : 96;
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
 
   __shared__ __attribute__((aligned(1024))) f16 smem[NS * STAGE];
@@ -162,7 +177,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     const int r = (is_w ? s - INS_A * 64 : s) >> 3, p = s & 7;
     const int c = p ^ ((r >> 1) & 7);
     int row;
-    if (is_w) row = w_row_mfma<EPI, BN>(a, tn, r);
+    if (is_w) row = w_row_mfma<EPI, BN, HD>(a, tn, r);
     else row = m0 + r < a.M ? m0 + r : a.M - 1;
     src_off[t] = row * K + c * 8;
     src_is_w[t] = is_w;
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < CB8; ++i) {
     const int q = tid + i * NT, r = q >> 2, c = q & 3;
-    w8_off[i] = w_row_mfma<EPI, BN>(a, tn, r) * K + c * 16;
+    w8_off[i] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 16;
   }
   i32x4 rw8[CB8 > 0 ? CB8 : 1];
 
@@ -277,7 +292,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     sc[j] = 1.0f;
-    if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN>(a, tn, wn * WN + j * 32 + col_l)];
+    if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN, HD>(a, tn, wn * WN + j * 32 + col_l)];
   }
 
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_PARTIAL) {
@@ -312,37 +327,50 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
         }
     }
   } else {  // EPI_QKV
-    // RoPE on the accumulators, then the wave's WM x 96 head tile goes through
+    // RoPE on the accumulators, then the wave's WM x HD head tile goes through
     // LDS in natural d order and leaves as 16-byte stores: rows of Q / K, and
-    // rows of V^T (64 tokens = 128 B per row segment).
-    constexpr int QLD = 104;              // Q/K staging row stride (conflict-free writes)
+    // rows of V^T (8-token chunks of one d row).
+    constexpr int HALF = HD / 2;
+    constexpr int QLD = HD + 8;           // Q/K staging row stride (conflict-free writes)
     constexpr int VLD = WM + 8;           // V^T staging row stride
-    constexpr int REG = (WM * QLD > 96 * VLD) ? WM * QLD : 96 * VLD;
+    constexpr int REG = (WM * QLD > HD * VLD) ? WM * QLD : HD * VLD;
     static_assert(NW * REG <= NS * STAGE, "QKV staging fits in the stage buffers");
-    const int col0 = tn * BN + wn * 96;   // first fused row of this wave's head
-    const int q_end = a.nh * 96, k_end = (a.nh + a.nkv) * 96;
+    const int col0 = tn * BN + wn * HD;   // first fused row of this wave's head
+    const int q_end = a.nh * HD, k_end = (a.nh + a.nkv) * HD;
     const bool is_v = col0 >= k_end;
-    const int head = col0 < q_end ? col0 / 96 : (col0 < k_end ? (col0 - q_end) / 96 : (col0 - k_end) / 96);
+    const int head = col0 < q_end ? col0 / HD : (col0 < k_end ? (col0 - q_end) / HD : (col0 - k_end) / HD);
     const int nheads = col0 < q_end ? a.nh : a.nkv;
-    const int d0 = col_l, d1 = 48 + col_l, d2 = col_l < 16 ? 32 + col_l : 64 + col_l;
-    const int f2 = 32 + (col_l & 15);  // frequency index of the third block's pair
+    // natural d of each accumulator block for this lane, and the frequency of
+    // the pair the block belongs to (blocks 0, 1 and, for HD = 128, 2, 3 pair up)
+    int dd[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) dd[j] = qkv_head_row<HD>(j * 32 + col_l);
+    const int fA = col_l;                                            // blocks 0, 1
+    const int fB = HD == 96 ? 32 + (col_l & 15) : 32 + col_l;        // block 2 (and 3)
     const int mw0 = m0 + wm * WM;      // first token row of this wave
     // rotation factors of the lane's rows: all loads in flight at once, before
-    // the barrier (position s = token row mod S, from one division per lane)
-    float c0[TM][16], s0[TM][16], c2[TM][16], s2[TM][16];
+    // the barrier.  Position = pos[row] when given, else row mod S.
+    float cA[TM][16], sA[TM][16], cB[TM][16], sB[TM][16];
     if (!is_v && col0 < a.N) {
       const int s_base = mw0 - (mw0 / a.S) * a.S;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          int sp = s_base + i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
-          while (sp >= a.S) sp -= a.S;
-          const size_t t = (size_t)sp * 48;
-          c0[i][v] = a.rope_cos[t + col_l];
-          s0[i][v] = a.rope_sin[t + col_l];
-          c2[i][v] = a.rope_cos[t + f2];
-          s2[i][v] = a.rope_sin[t + f2];
+          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+          int sp;
+          if (a.pos) {
+            sp = a.pos[min(mw0 + r, a.M - 1)];
+            sp = sp < 0 ? 0 : (sp >= a.max_pos ? a.max_pos - 1 : sp);
+          } else {
+            sp = s_base + r;
+            while (sp >= a.S) sp -= a.S;
+          }
+          const size_t t = (size_t)sp * HALF;
+          cA[i][v] = a.rope_cos[t + fA];
+          sA[i][v] = a.rope_sin[t + fA];
+          cB[i][v] = a.rope_cos[t + fB];
+          sB[i][v] = a.rope_sin[t + fB];
         }
     }
     __syncthreads();                      // every wave is done with the k-stages
@@ -354,9 +382,8 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
-          tile[d0 * VLD + r] = (f16)(acc[i][0][v] * sc[0]);
-          tile[d1 * VLD + r] = (f16)(acc[i][1][v] * sc[1]);
-          tile[d2 * VLD + r] = (f16)(acc[i][2][v] * sc[2]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) tile[dd[j] * VLD + r] = (f16)(acc[i][j][v] * sc[j]);
         }
     } else {
 #pragma unroll
@@ -364,42 +391,50 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
-          const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1], y2 = acc[i][2][v] * sc[2];
-          const float y2p = __shfl_xor(y2, 16);  // partner of the third block
-          tile[r * QLD + d0] = (f16)(y0 * c0[i][v] - y1 * s0[i][v]);
-          tile[r * QLD + d1] = (f16)(y1 * c0[i][v] + y0 * s0[i][v]);
-          tile[r * QLD + d2] = (f16)(col_l < 16 ? y2 * c2[i][v] - y2p * s2[i][v] : y2 * c2[i][v] + y2p * s2[i][v]);
+          const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1];
+          tile[r * QLD + dd[0]] = (f16)(y0 * cA[i][v] - y1 * sA[i][v]);
+          tile[r * QLD + dd[1]] = (f16)(y1 * cA[i][v] + y0 * sA[i][v]);
+          if constexpr (HD == 96) {
+            const float y2 = acc[i][2][v] * sc[2];
+            const float y2p = __shfl_xor(y2, 16);  // partner of the third block
+            tile[r * QLD + dd[2]] = (f16)(col_l < 16 ? y2 * cB[i][v] - y2p * sB[i][v] : y2 * cB[i][v] + y2p * sB[i][v]);
+          } else {
+            const float y2 = acc[i][2][v] * sc[2], y3 = acc[i][3][v] * sc[3];
+            tile[r * QLD + dd[2]] = (f16)(y2 * cB[i][v] - y3 * sB[i][v]);
+            tile[r * QLD + dd[3]] = (f16)(y3 * cB[i][v] + y2 * sB[i][v]);
+          }
         }
     }
     // the wave reads back only what it wrote: its own LDS operations are ordered
     if (!is_v) {
       f16* dst = reinterpret_cast<f16*>(col0 < q_end ? a.q : a.k);
-      for (int idx = lane; idx < WM * 12; idx += 64) {
-        const int r = idx / 12, c = idx - r * 12;
+      constexpr int CR = HD / 8;  // 16-byte chunks per row
+      for (int idx = lane; idx < WM * CR; idx += 64) {
+        const int r = idx / CR, c = idx - r * CR;
         const int m = mw0 + r;
         if (m >= a.M) continue;
         const int b = m / a.S, s = m - b * a.S;
-        *reinterpret_cast<f16x8*>(dst + ((size_t)(b * nheads + head) * a.S + s) * 96 + c * 8) =
+        *reinterpret_cast<f16x8*>(dst + ((size_t)(b * nheads + head) * a.S + s) * HD + c * 8) =
             *reinterpret_cast<const f16x8*>(tile + r * QLD + c * 8);
       }
     } else {
       f16* vt = reinterpret_cast<f16*>(a.vt);
       constexpr int CPR = WM / 8;  // 8-token chunks per V^T row segment
-      const bool aligned = (a.S & 7) == 0;  // then a chunk never straddles two sequences
-      for (int idx = lane; idx < 96 * CPR; idx += 64) {
+      const bool aligned = (a.S & 7) == 0 && (a.s_pad & 7) == 0;  // chunks never straddle sequences
+      for (int idx = lane; idx < HD * CPR; idx += 64) {
         const int d = idx / CPR, c = idx - d * CPR;
         const int m = mw0 + c * 8;
         if (m >= a.M) continue;
         if (aligned) {
           const int b = m / a.S, s = m - b * a.S;
-          *reinterpret_cast<f16x8*>(vt + ((size_t)(b * a.nkv + head) * 96 + d) * a.s_pad + s) =
+          *reinterpret_cast<f16x8*>(vt + ((size_t)(b * a.nkv + head) * HD + d) * a.s_pad + s) =
               *reinterpret_cast<const f16x8*>(tile + d * VLD + c * 8);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if (m + e >= a.M) break;
             const int b = (m + e) / a.S, s = m + e - b * a.S;
-            vt[((size_t)(b * a.nkv + head) * 96 + d) * a.s_pad + s] = tile[d * VLD + c * 8 + e];
+            vt[((size_t)(b * a.nkv + head) * HD + d) * a.s_pad + s] = tile[d * VLD + c * 8 + e];
           }
         }
       }

@@ -23,7 +23,7 @@ struct NormArgs {
 };
 
 constexpr int kNormThreads = 256;
-constexpr int kNormMaxChunks = 4;  // hidden <= 4 * 4 * 256 = 4096
+constexpr int kNormMaxChunks = 8;  // hidden <= 8 * 4 * 256 = 8192
 
 // Sum over the workgroup (4 waves) via LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {

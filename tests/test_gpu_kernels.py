@@ -91,10 +91,10 @@ def test_gate_up_silu_epilogue(phi, wtype, M, I, K):
     assert np.all(np.abs(got - ref) <= tol * (1 + np.abs(ref))), np.abs(got - ref).max()
 
 
-def _attn_inputs(B, S, nh, nkv, dtype, seed, scale=1.0):
-    q = synth.normal(seed, "attn.q", (B, nh, S, 96), scale, dtype)
-    k = synth.normal(seed, "attn.k", (B, nkv, S, 96), scale, dtype)
-    v = synth.normal(seed, "attn.v", (B, nkv, S, 96), 1.0, dtype)
+def _attn_inputs(B, S, nh, nkv, dtype, seed, scale=1.0, D=96):
+    q = synth.normal(seed, "attn.q", (B, nh, S, D), scale, dtype)
+    k = synth.normal(seed, "attn.k", (B, nkv, S, D), scale, dtype)
+    v = synth.normal(seed, "attn.v", (B, nkv, S, D), 1.0, dtype)
     return q, k, v
 
 
@@ -128,6 +128,16 @@ def _attn_ref(q, k, v):
 def test_attention_f16_peaked(phi, B, S, nh, nkv):
     _say(f"attention f16 B={B} S={S} nh={nh} nkv={nkv}")
     q, k, v = _attn_inputs(B, S, nh, nkv, np.float16, 21 + S, scale=1.5)
+    got = _attn_gpu(phi, q, k, v)
+    ref = _attn_ref(q, k, v)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 2e-3 + 2e-3 * np.abs(ref)), np.abs(got - ref).max()
+
+
+@pytest.mark.parametrize("B,S,nh,nkv", [(1, 1, 4, 1), (1, 31, 8, 2), (2, 100, 8, 2), (1, 513, 40, 10)])
+def test_attention_f16_head_dim_128(phi, B, S, nh, nkv):
+    _say(f"attention f16 D=128 B={B} S={S} nh={nh} nkv={nkv}")
+    q, k, v = _attn_inputs(B, S, nh, nkv, np.float16, 41 + S, scale=1.5, D=128)
     got = _attn_gpu(phi, q, k, v)
     ref = _attn_ref(q, k, v)
     assert np.all(np.isfinite(got))
