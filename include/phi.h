@@ -243,6 +243,52 @@ phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_
                            int32_t page_size, int32_t n_pages, int32_t max_pages, void* k_pool, void* v_pool,
                            void* stream);
 
+/* ---- K16/V8 cached decoding of a loaded model ([P3]) ------------------------
+ * A paged cache for every layer: keys binary16, values E4M3 with a float32
+ * scale per (layer, KV head) ([P3] setup paragraph), 16-token pages shared by
+ * the sequences of a batch through one block table.  All device memory is
+ * the caller's; the two pointer arrays are host arrays.
+ *   k_pools[l]  binary16 [n_pages][n_kv_heads][16][head_dim], layer l
+ *   v_pools[l]  uint8    [n_pages][n_kv_heads][16][head_dim], layer l
+ *   v_scale     float32  [n_layers][n_kv_heads] (device)
+ *   block_table int32    [batch][max_pages] (device): token t of sequence b
+ *               is in page block_table[b][t / 16], slot t % 16
+ * Models: head_dim 128, n_heads / n_kv_heads in {1, 2, 4, 8}, binary16 or
+ * int8 weights. */
+typedef struct {
+  void* const* k_pools;
+  void* const* v_pools;
+  const float* v_scale;
+  const int32_t* block_table;
+  int32_t n_pages, max_pages, page_size;
+} phi_kv_cache;
+
+/* phi_prefill_logits, and in addition every layer's keys and values of
+ * tokens 0..seq-1 of each sequence are written into the cache with the
+ * encoding of kv_append_k16v8 (the prefill's own attention uses them
+ * unquantised).  seq <= max_pages * 16 (PHI_E_RANGE otherwise).  Workspace:
+ * phi_workspace_bytes(m, batch, seq). */
+phi_status phi_prefill_fill_k16v8(const phi_model* m, const int32_t* ids, int32_t batch, int32_t seq,
+                                  float* logits, const phi_kv_cache* cache, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* One decode step: sequence b's token ids[b] at position positions[b] (its
+ * cache length; both device int32 [batch]) goes through every layer - RMSNorm,
+ * fused QKV with RoPE at that position, the cache write of its key and value
+ * (kv_append_k16v8), decode attention over positions[b] + 1 cached tokens
+ * (attn_decode_k16v8), o_proj, RMSNorm, fused gate/up, down - and the final
+ * RMSNorm and lm_head give logits float32 [batch][vocab].  max_ctx bounds
+ * positions[b] + 1 for every b (1 <= max_ctx <= max_pages * 16 and
+ * <= max_pos; PHI_E_RANGE otherwise).  Device-side values are checked in the
+ * kernels: a position whose slot lies outside the table or pool is not
+ * written, and a cache length outside [1, max_pages * 16] makes that
+ * sequence's attention output NaN.  Workspace:
+ * phi_decode_workspace_bytes(m, batch, max_ctx). */
+size_t phi_decode_workspace_bytes(const phi_model* m, int32_t batch, int32_t max_ctx);
+phi_status phi_decode_step_k16v8(const phi_model* m, const int32_t* ids, const int32_t* positions, int32_t batch,
+                                 int32_t max_ctx, const phi_kv_cache* cache, float* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Token slots per layer of a KV pool of budget_bytes split evenly over
  * n_layers, each token holding one key of k_bytes and one value of v_bytes per
  * element per KV head, rounded down to whole pages ([P3] pool paragraph:

@@ -23,7 +23,8 @@ WTYPES = {"f32": PHI_WT_F32, "f16": PHI_WT_F16, "i8": PHI_WT_I8}
 EXPORTS = ("phi_state_bytes", "phi_load_fused", "phi_workspace_bytes", "phi_prefill_logits", "phi_free",
            "phi_strerror", "phi_linear_f32out", "phi_gate_up_silu", "phi_attention_vt_stride", "phi_attention_prefill",
            "attn_decode_k16v8_workspace_bytes", "attn_decode_k16v8", "phi_kv_pool_slots", "phi_profile_enable",
-           "phi_profile_read", "kv_append_k16v8")
+           "phi_profile_read", "kv_append_k16v8", "phi_prefill_fill_k16v8", "phi_decode_workspace_bytes",
+           "phi_decode_step_k16v8")
 
 
 class PhiError(RuntimeError):
@@ -41,6 +42,12 @@ class phi_config(ctypes.Structure):
 
 class phi_linear(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class phi_kv_cache(ctypes.Structure):
+    _fields_ = [("k_pools", ctypes.POINTER(ctypes.c_void_p)), ("v_pools", ctypes.POINTER(ctypes.c_void_p)),
+                ("v_scale", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32)]
 
 
 class phi_layer_weights(ctypes.Structure):
@@ -79,6 +86,9 @@ def lib() -> ctypes.CDLL:
         "attn_decode_k16v8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "attn_decode_k16v8": (i32, [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, sz, P]),
         "kv_append_k16v8": (i32, [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]),
+        "phi_prefill_fill_k16v8": (i32, [P, P, i32, i32, P, ctypes.POINTER(phi_kv_cache), P, sz, P]),
+        "phi_decode_workspace_bytes": (sz, [P, i32, i32]),
+        "phi_decode_step_k16v8": (i32, [P, P, P, i32, i32, ctypes.POINTER(phi_kv_cache), P, P, sz, P]),
         "phi_kv_pool_slots": (i64, [i64, i32, i32, i32, i32, i32, i32]),
         "phi_profile_enable": (i32, [P, i32]),
         "phi_profile_read": (i32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -149,6 +159,39 @@ class Model:
     def prefill_logits(self, ids, logits=None, workspace=None, stream=None):
         return phi_prefill_logits(self, ids, logits, workspace, stream)
 
+    def prefill_fill_k16v8(self, ids, cache: "KVCache", logits=None, workspace=None, stream=None):
+        """Prefill logits [B, S, V] that also writes every layer's keys and
+        values of the B sequences into `cache` (pages from its block table)."""
+        import torch
+        B, S = ids.shape
+        if ids.dtype != torch.int32 or not ids.is_contiguous():
+            raise ValueError("ids must be a contiguous int32 tensor")
+        if logits is None:
+            logits = torch.empty((B, S, self.cfg.vocab), dtype=torch.float32, device=ids.device)
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes(B, S), dtype=torch.uint8, device=ids.device)
+        c = cache.struct()
+        _check(lib().phi_prefill_fill_k16v8(self.handle, _ptr(ids), B, S, _ptr(logits), ctypes.byref(c),
+                                            _ptr(workspace), workspace.numel(), _stream(stream)),
+               "phi_prefill_fill_k16v8")
+        return logits
+
+    def decode_step_k16v8(self, ids, positions, cache: "KVCache", max_ctx: int, logits=None, workspace=None,
+                          stream=None):
+        """One decode step: ids, positions int32 device [B] -> logits [B, V]."""
+        import torch
+        B = ids.shape[0]
+        if logits is None:
+            logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=ids.device)
+        if workspace is None:
+            need = lib().phi_decode_workspace_bytes(self.handle, B, max_ctx)
+            workspace = torch.empty(need, dtype=torch.uint8, device=ids.device)
+        c = cache.struct()
+        _check(lib().phi_decode_step_k16v8(self.handle, _ptr(ids), _ptr(positions), B, max_ctx, ctypes.byref(c),
+                                           _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream)),
+               "phi_decode_step_k16v8")
+        return logits
+
     def profile_enable(self, enable: bool = True):
         _check(lib().phi_profile_enable(self.handle, int(enable)), "phi_profile_enable")
 
@@ -164,6 +207,37 @@ class Model:
         if h is not None and _lib is not None:
             _lib.phi_free(h)
             self.handle = None
+
+
+class KVCache:
+    """Device tensors of a K16/V8 paged cache for every layer (see
+    phi_kv_cache in include/phi.h): k_pools / v_pools lists of
+    [n_pages, n_kv_heads, 16, head_dim] binary16 / uint8 tensors, v_scale
+    float32 [n_layers, n_kv_heads], block_table int32 [B, max_pages]."""
+
+    def __init__(self, k_pools, v_pools, v_scale, block_table):
+        self.k_pools, self.v_pools = list(k_pools), list(v_pools)
+        self.v_scale, self.block_table = v_scale, block_table
+
+    @classmethod
+    def empty(cls, cfg, n_pages: int, block_table, v_scale, device="cuda"):
+        import torch
+        shape = (n_pages, cfg.n_kv_heads, 16, cfg.head_dim)
+        k = [torch.zeros(shape, dtype=torch.float16, device=device) for _ in range(cfg.n_layers)]
+        v = [torch.zeros(shape, dtype=torch.uint8, device=device) for _ in range(cfg.n_layers)]
+        return cls(k, v, v_scale, block_table)
+
+    def struct(self, block_table=None) -> phi_kv_cache:
+        bt = self.block_table if block_table is None else block_table
+        self._kp = (ctypes.c_void_p * len(self.k_pools))(*[t.data_ptr() for t in self.k_pools])
+        self._vp = (ctypes.c_void_p * len(self.v_pools))(*[t.data_ptr() for t in self.v_pools])
+        return phi_kv_cache(ctypes.cast(self._kp, ctypes.POINTER(ctypes.c_void_p)),
+                            ctypes.cast(self._vp, ctypes.POINTER(ctypes.c_void_p)), self.v_scale.data_ptr(),
+                            bt.data_ptr(), self.k_pools[0].shape[0], bt.shape[1], 16)
+
+    def with_table(self, block_table) -> "KVCache":
+        """The same pools seen through another block table (e.g. one row)."""
+        return KVCache(self.k_pools, self.v_pools, self.v_scale, block_table)
 
 
 def phi_load_fused(cfg, weights: dict, stream=None) -> Model:

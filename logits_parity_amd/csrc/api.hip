@@ -258,9 +258,30 @@ struct StageTimer {
 // Launch slots of one forward: embed + per layer (qkv, attn, o, norm, gate_up, down, norm) + lm_head.
 inline size_t launches_per_forward(const phi_config& c) { return 2 + 7 * (size_t)c.n_layers; }
 
+// Cache fill of layer l from the QKV outputs in the prefill workspace.
+phi_status kv_fill(const phi_kv_cache* cache, int l, const void* k, const void* vt, int batch, int seq, int s_pad,
+                   int n_kv_heads, hipStream_t st) {
+  KvFillArgs f{};
+  f.k = reinterpret_cast<const f16*>(k);
+  f.vt = reinterpret_cast<const f16*>(vt);
+  f.v_scale = cache->v_scale + (size_t)l * n_kv_heads;
+  f.block_table = cache->block_table;
+  f.k_pool = reinterpret_cast<f16*>(cache->k_pools[l]);
+  f.v_pool = reinterpret_cast<uint8_t*>(cache->v_pools[l]);
+  f.B = batch;
+  f.Hkv = n_kv_heads;
+  f.S = seq;
+  f.s_pad = s_pad;
+  f.n_pages = cache->n_pages;
+  f.max_pages = cache->max_pages;
+  const size_t threads = (size_t)batch * n_kv_heads * seq * 16;
+  hipLaunchKernelGGL(phi_kv_fill_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, f);
+  return launched();
+}
+
 template <class AT>
 phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, float* logits, char* ws,
-                   hipStream_t st) {
+                   hipStream_t st, const phi_kv_cache* cache = nullptr) {
   StageTimer tm{const_cast<PhiProfile*>(&m->prof), st};
   const phi_config& c = m->cfg;
   const PrefillPlan p = plan_prefill(c, batch, seq);
@@ -322,6 +343,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.vt = const_cast<void*>(aa.vt);
     tm.begin(PHI_PROF_QKV);
     s = gemm<EPI_QKV>(wt, g, p.qkv, st);
+    if (!s && cache) s = kv_fill(cache, l, aa.k, aa.vt, batch, seq, p.s_pad, c.n_kv_heads, st);
     tm.end();
     if (s) return s;
 
@@ -421,6 +443,229 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
   return p;
 }
 
+
+// Launch of split-KV decode attention + merge (arguments already checked).
+phi_status decode_attention(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
+                            const int32_t* block_table, const int32_t* ctx_lens, int batch, int n_q_heads,
+                            int n_kv_heads, int n_pages, int max_pages, float sm_scale, void* out, void* workspace,
+                            const DecodePlan& p, hipStream_t st) {
+  DecodeArgs a{};
+  a.q = reinterpret_cast<const f16*>(q);
+  a.k_pool = reinterpret_cast<const f16*>(k_pool);
+  a.v_pool = reinterpret_cast<const uint8_t*>(v_pool);
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + p.off_ml);
+  a.out = reinterpret_cast<f16*>(out);
+  a.B = batch;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.n_pages = n_pages;
+  a.max_pages = max_pages;
+  a.n_split = p.n_split;
+  a.pages_per_split = p.pages_per_split;
+  a.scale_log2 = sm_scale * kLog2e;
+  const dim3 grid(p.n_split, n_kv_heads, batch);
+  switch (n_q_heads / n_kv_heads) {
+    case 1: hipLaunchKernelGGL(phi_decode_split_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(phi_decode_split_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(phi_decode_split_kernel<4>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(phi_decode_split_kernel<8>, grid, dim3(256), 0, st, a); break;
+  }
+  if (hipGetLastError() != hipSuccess) return PHI_E_HIP;
+  hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
+  return launched();
+}
+
+// Launch of the one-token cache write (arguments already checked, batch >= 1).
+phi_status kv_append(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,
+                     const int32_t* positions, int batch, int n_kv_heads, int n_pages, int max_pages, void* k_pool,
+                     void* v_pool, hipStream_t st) {
+  KvAppendArgs a{};
+  a.k_new = reinterpret_cast<const f16*>(k_new);
+  a.v_new = reinterpret_cast<const f16*>(v_new);
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.positions = positions;
+  a.k_pool = reinterpret_cast<f16*>(k_pool);
+  a.v_pool = reinterpret_cast<uint8_t*>(v_pool);
+  a.B = batch;
+  a.Hkv = n_kv_heads;
+  a.n_pages = n_pages;
+  a.max_pages = max_pages;
+  const int rows = batch * n_kv_heads;
+  hipLaunchKernelGGL(phi_kv_append_kernel, dim3((rows + 15) / 16), dim3(256), 0, st, a);
+  return launched();
+}
+
+// ---------------------------------------------------------------- decode step
+struct DecodeStepPlan {
+  GemmPlan qkv, o, gu, down, lm;
+  DecodePlan att;
+  size_t off_x, off_xn, off_q, off_k, off_v, off_attn, off_act, off_part, off_ctx, off_att, total;
+};
+
+DecodeStepPlan plan_decode_step(const phi_config& c, int batch, int max_ctx) {
+  DecodeStepPlan p;
+  const int B = batch, H = c.hidden, hd = c.head_dim, I = c.intermediate;
+  const bool w8 = c.wtype == PHI_WT_I8;
+  p.qkv = plan_gemm(EPI_QKV, B, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8, hd);
+  p.o = plan_gemm(EPI_RESID, B, H, c.n_heads * hd, w8);
+  p.gu = plan_gemm(EPI_SILU, B, 2 * I, H, w8);
+  p.down = plan_gemm(EPI_RESID, B, H, I, w8);
+  p.lm = plan_gemm(EPI_F32, B, c.vocab, H, w8);
+  p.att = plan_decode(B, c.n_heads, c.n_kv_heads, max_ctx);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = round_up(o + bytes, 256); return r; };
+  p.off_x = take((size_t)B * H * 4);
+  p.off_xn = take((size_t)B * H * 2);
+  p.off_q = take((size_t)B * c.n_heads * hd * 2);
+  p.off_k = take((size_t)B * c.n_kv_heads * hd * 2);
+  p.off_v = take((size_t)B * c.n_kv_heads * hd * 2);
+  p.off_attn = take((size_t)B * c.n_heads * hd * 2);
+  p.off_act = take((size_t)B * I * 2);
+  const int max_split = std::max(p.o.splits, p.down.splits);
+  p.off_part = take(max_split > 1 ? (size_t)max_split * B * H * 4 : 0);
+  p.off_ctx = take((size_t)B * 4);
+  p.off_att = take(p.att.total);
+  p.total = o;
+  return p;
+}
+
+// One token per sequence through every layer with the K16/V8 cache.  The
+// QKV GEMM sees S = 1 (each row its own sequence) and s_pad = 1, so its
+// V^T output is the row-major [B][n_kv_heads][hd] that the cache write takes.
+phi_status decode_step(const phi_model* m, const int32_t* ids, const int32_t* positions, int batch, int max_ctx,
+                       const phi_kv_cache* cache, float* logits, char* ws, hipStream_t st) {
+  const phi_config& c = m->cfg;
+  const DecodeStepPlan p = plan_decode_step(c, batch, max_ctx);
+  const int B = batch, H = c.hidden, I = c.intermediate, hd = c.head_dim;
+  float* x = reinterpret_cast<float*>(ws + p.off_x);
+  void* xn = ws + p.off_xn;
+  void* q = ws + p.off_q;
+  void* k = ws + p.off_k;
+  void* v = ws + p.off_v;
+  void* attn = ws + p.off_attn;
+  void* act = ws + p.off_act;
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  int32_t* ctx = reinterpret_cast<int32_t*>(ws + p.off_ctx);
+  const int wt = c.wtype;
+
+  hipLaunchKernelGGL(phi_ctx_from_pos_kernel, dim3((B + 255) / 256), dim3(256), 0, st, positions, ctx, B);
+  phi_status s = launched();
+  if (s) return s;
+
+  NormArgs na{};
+  na.ids = ids;
+  na.embed = m->embed;
+  na.x = x;
+  na.xn = xn;
+  na.part = part;
+  na.T = B;
+  na.H = H;
+  na.V = c.vocab;
+  na.eps = c.rms_eps;
+  na.gain = m->layers[0].ln1;
+  if ((s = norm<f16, f16>(true, na, st))) return s;
+
+  GemmArgs base{};
+  base.M = B;
+  base.S = 1;
+  base.s_pad = 1;
+  base.nh = c.n_heads;
+  base.nkv = c.n_kv_heads;
+  base.hd = hd;
+  base.rope_cos = m->rope_cos;
+  base.rope_sin = m->rope_sin;
+  base.pos = positions;
+  base.max_pos = c.max_pos;
+  const float sm_scale = 1.0f / sqrtf((float)hd);
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const phi_layer_weights& L = m->layers[l];
+    GemmArgs g = base;
+    g.A = xn;
+    g.W = L.qkv.w;
+    g.scale = L.qkv.scale;
+    g.N = (c.n_heads + 2 * c.n_kv_heads) * hd;
+    g.K = H;
+    g.q = q;
+    g.k = k;
+    g.vt = v;
+    if ((s = gemm<EPI_QKV>(wt, g, p.qkv, st))) return s;
+    const float* vs = cache->v_scale + (size_t)l * c.n_kv_heads;
+    if ((s = kv_append(k, v, vs, cache->block_table, positions, B, c.n_kv_heads, cache->n_pages,
+                       cache->max_pages, cache->k_pools[l], cache->v_pools[l], st)))
+      return s;
+    if ((s = decode_attention(q, cache->k_pools[l], cache->v_pools[l], vs, cache->block_table, ctx, B, c.n_heads,
+                              c.n_kv_heads, cache->n_pages, cache->max_pages, sm_scale, attn, ws + p.off_att,
+                              p.att, st)))
+      return s;
+
+    g = base;
+    g.A = attn;
+    g.W = L.o.w;
+    g.scale = L.o.scale;
+    g.N = H;
+    g.K = c.n_heads * hd;
+    g.x = x;
+    g.ldx = H;
+    g.out = part;
+    if ((s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit))) return s;
+    na.gain = L.ln2;
+    if ((s = norm<f16, f16>(false, na, st))) return s;
+
+    g = base;
+    g.A = xn;
+    g.W = L.gate_up.w;
+    g.scale = L.gate_up.scale;
+    g.N = 2 * I;
+    g.K = H;
+    g.act = act;
+    g.ld_act = I;
+    if ((s = gemm<EPI_SILU>(wt, g, p.gu, st))) return s;
+
+    g = base;
+    g.A = act;
+    g.W = L.down.w;
+    g.scale = L.down.scale;
+    g.N = H;
+    g.K = I;
+    g.x = x;
+    g.ldx = H;
+    g.out = part;
+    if ((s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit))) return s;
+    na.gain = l + 1 < c.n_layers ? m->layers[l + 1].ln1 : m->final_norm;
+    if ((s = norm<f16, f16>(false, na, st))) return s;
+  }
+
+  GemmArgs g = base;
+  g.A = xn;
+  g.W = m->lm_head.w;
+  g.scale = m->lm_head.scale;
+  g.N = c.vocab;
+  g.K = H;
+  g.out = logits;
+  g.ldo = c.vocab;
+  return gemm<EPI_F32>(wt, g, p.lm, st);
+}
+
+// Model and cache checks shared by the cached entry points.
+phi_status check_cache(const phi_model* m, const phi_kv_cache* cache) {
+  const phi_config& c = m->cfg;
+  const int G = c.n_heads / c.n_kv_heads;
+  if (c.head_dim != 128 || c.wtype == PHI_WT_F32 || (G != 1 && G != 2 && G != 4 && G != 8)) return PHI_E_SHAPE;
+  if (!cache->k_pools || !cache->v_pools || !cache->v_scale || !cache->block_table) return PHI_E_NULL;
+  if (cache->page_size != 16 || cache->n_pages < 1 || cache->max_pages < 1) return PHI_E_SHAPE;
+  if ((long long)cache->n_pages * c.n_kv_heads * 16 * 128 * 2 > (1ll << 40)) return PHI_E_SHAPE;
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!cache->k_pools[l] || !cache->v_pools[l]) return PHI_E_NULL;
+    if (!aligned16(cache->k_pools[l]) || !aligned16(cache->v_pools[l])) return PHI_E_ALIGN;
+  }
+  return PHI_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -641,35 +886,8 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
   if (workspace_bytes < p.total) return PHI_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
     return PHI_E_ALIGN;
-  DecodeArgs a{};
-  a.q = reinterpret_cast<const f16*>(q);
-  a.k_pool = reinterpret_cast<const f16*>(k_pool);
-  a.v_pool = reinterpret_cast<const uint8_t*>(v_pool);
-  a.v_scale = v_scale;
-  a.block_table = block_table;
-  a.ctx_lens = ctx_lens;
-  a.part_o = reinterpret_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + p.off_ml);
-  a.out = reinterpret_cast<f16*>(out);
-  a.B = batch;
-  a.Hq = n_q_heads;
-  a.Hkv = n_kv_heads;
-  a.n_pages = n_pages;
-  a.max_pages = max_pages;
-  a.n_split = p.n_split;
-  a.pages_per_split = p.pages_per_split;
-  a.scale_log2 = sm_scale * kLog2e;
-  hipStream_t st = as_stream(stream);
-  const dim3 grid(p.n_split, n_kv_heads, batch);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(phi_decode_split_kernel<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(phi_decode_split_kernel<2>, grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(phi_decode_split_kernel<4>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(phi_decode_split_kernel<8>, grid, dim3(256), 0, st, a); break;
-  }
-  if (hipGetLastError() != hipSuccess) return PHI_E_HIP;
-  hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
-  return launched();
+  return decode_attention(q, k_pool, v_pool, v_scale, block_table, ctx_lens, batch, n_q_heads, n_kv_heads,
+                          n_pages, max_pages, sm_scale, out, workspace, p, as_stream(stream));
 }
 
 phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,
@@ -683,21 +901,44 @@ phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_
   if ((long long)n_pages * n_kv_heads * 16 * 128 * 2 > (1ll << 40) || (long long)batch * n_kv_heads > (1 << 26))
     return PHI_E_SHAPE;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)) return PHI_E_ALIGN;
-  KvAppendArgs a{};
-  a.k_new = reinterpret_cast<const f16*>(k_new);
-  a.v_new = reinterpret_cast<const f16*>(v_new);
-  a.v_scale = v_scale;
-  a.block_table = block_table;
-  a.positions = positions;
-  a.k_pool = reinterpret_cast<f16*>(k_pool);
-  a.v_pool = reinterpret_cast<uint8_t*>(v_pool);
-  a.B = batch;
-  a.Hkv = n_kv_heads;
-  a.n_pages = n_pages;
-  a.max_pages = max_pages;
-  const int rows = batch * n_kv_heads;
-  hipLaunchKernelGGL(phi_kv_append_kernel, dim3((rows + 15) / 16), dim3(256), 0, as_stream(stream), a);
-  return launched();
+  return kv_append(k_new, v_new, v_scale, block_table, positions, batch, n_kv_heads, n_pages, max_pages, k_pool,
+                   v_pool, as_stream(stream));
+}
+
+
+phi_status phi_prefill_fill_k16v8(const phi_model* m, const int32_t* ids, int32_t batch, int32_t seq,
+                                  float* logits, const phi_kv_cache* cache, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!m || !ids || !logits || !workspace || !cache) return PHI_E_NULL;
+  phi_status s = check_cache(m, cache);
+  if (s) return s;
+  if (batch < 1 || seq < 1) return PHI_E_SHAPE;
+  if (seq > m->cfg.max_pos || seq > cache->max_pages * 16) return PHI_E_RANGE;
+  if ((long long)batch * seq > (1 << 24)) return PHI_E_SHAPE;
+  if (workspace_bytes < plan_prefill(m->cfg, batch, seq).total) return PHI_E_WORKSPACE;
+  if (!aligned16(ids) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
+  const PhiProfile& pr = m->prof;
+  if (pr.enabled && pr.used + launches_per_forward(m->cfg) > pr.stage.size()) return PHI_E_RANGE;
+  return forward<f16>(m, ids, batch, seq, logits, reinterpret_cast<char*>(workspace), as_stream(stream), cache);
+}
+
+size_t phi_decode_workspace_bytes(const phi_model* m, int32_t batch, int32_t max_ctx) {
+  if (!m || batch < 1 || max_ctx < 1 || m->cfg.head_dim != 128) return 0;
+  return plan_decode_step(m->cfg, batch, max_ctx).total;
+}
+
+phi_status phi_decode_step_k16v8(const phi_model* m, const int32_t* ids, const int32_t* positions, int32_t batch,
+                                 int32_t max_ctx, const phi_kv_cache* cache, float* logits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!m || !ids || !positions || !logits || !workspace || !cache) return PHI_E_NULL;
+  phi_status s = check_cache(m, cache);
+  if (s) return s;
+  if (batch < 1 || batch > (1 << 16)) return PHI_E_SHAPE;
+  if (max_ctx < 1 || max_ctx > cache->max_pages * 16 || max_ctx > m->cfg.max_pos) return PHI_E_RANGE;
+  if (workspace_bytes < plan_decode_step(m->cfg, batch, max_ctx).total) return PHI_E_WORKSPACE;
+  if (!aligned16(ids) || !aligned16(positions) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
+  return decode_step(m, ids, positions, batch, max_ctx, cache, logits, reinterpret_cast<char*>(workspace),
+                     as_stream(stream));
 }
 
 int64_t phi_kv_pool_slots(int64_t budget_bytes, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,

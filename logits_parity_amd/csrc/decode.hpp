@@ -304,3 +304,57 @@ __global__ __launch_bounds__(256) void phi_kv_append_kernel(KvAppendArgs a) {
 }
 
 }  // namespace phi
+
+namespace phi {
+
+// ---- K16/V8 cache fill from a prefill ---------------------------------------
+// The prefill's post-RoPE keys [B][Hkv][S][128] and transposed values
+// V^T [B][Hkv][128][s_pad] (binary16, as the QKV GEMM leaves them) go to the
+// pages of every sequence, token t of sequence b at block_table[b][t / 16],
+// slot t % 16, with the value encoding of the single-token cache write.  One
+// thread moves 8 dims of one token: a 16-byte key copy and an 8-byte value
+// store (the 8 values are a column of V^T: 8 strided 2-byte loads).
+
+struct KvFillArgs {
+  const f16* k;       // [B][Hkv][S][128]
+  const f16* vt;      // [B][Hkv][128][s_pad]
+  const float* v_scale;
+  const int32_t* block_table;
+  f16* k_pool;
+  uint8_t* v_pool;
+  int B, Hkv, S, s_pad, n_pages, max_pages;
+};
+
+__global__ __launch_bounds__(256) void phi_kv_fill_kernel(KvFillArgs a) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)a.B * a.Hkv * a.S * 16;
+  if (idx >= total) return;
+  const int c = (int)(idx & 15);
+  const size_t row = idx >> 4;             // (b, g, t)
+  const int t = (int)(row % a.S);
+  const int bg = (int)(row / a.S);
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  if (t >= a.max_pages * 16) return;
+  const int page = a.block_table[(size_t)b * a.max_pages + (t >> 4)];
+  if (page < 0 || page >= a.n_pages) return;
+  const size_t dst = (((size_t)page * a.Hkv + g) * 16 + (t & 15)) * 128 + c * 8;
+  *reinterpret_cast<uint4*>(a.k_pool + dst) = *reinterpret_cast<const uint4*>(a.k + row * 128 + c * 8);
+  const f16* vcol = a.vt + ((size_t)bg * 128 + c * 8) * a.s_pad + t;
+  const float s = a.v_scale[g];
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = e4m3_operand(static_cast<float>(vcol[(size_t)e * a.s_pad]), s);
+  uint2 out;
+  out.x = e4m3_pack4(x[0], x[1], x[2], x[3]);
+  out.y = e4m3_pack4(x[4], x[5], x[6], x[7]);
+  *reinterpret_cast<uint2*>(a.v_pool + dst) = out;
+}
+
+// ctx[b] = pos[b] + 1: the cache length a decode step attends over once its
+// token is appended.
+__global__ void phi_ctx_from_pos_kernel(const int32_t* pos, int32_t* ctx, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) ctx[b] = pos[b] + 1;
+}
+
+}  // namespace phi

@@ -87,11 +87,11 @@ def _mlp_tail(x, a, lw, cfg):
     return x + linear(silu(gu[:, :I]) * gu[:, I:], lw["down"])
 
 
-def prefill_fill(cfg, weights, ids: np.ndarray, v_scale: np.ndarray, exact: bool = False):
+def prefill_fill(cfg, weights, ids: np.ndarray, v_scale: np.ndarray, exact: bool = False, logits: bool = True):
     """Prefill of one sequence (ids int [S]) that fills its cache.
 
-    Returns (logits fp64 [S, vocab], SeqCache, per-layer raw (k, v) fp64).
-    v_scale fp32 [n_layers, kv_heads]."""
+    Returns (logits fp64 [S, vocab] or None when logits=False, SeqCache,
+    per-layer raw (k, v) fp64).  v_scale fp32 [n_layers, kv_heads]."""
     ids = np.asarray(ids)
     S = ids.shape[0]
     x = widen(weights.embed[ids])
@@ -107,8 +107,11 @@ def prefill_fill(cfg, weights, ids: np.ndarray, v_scale: np.ndarray, exact: bool
         cache.layers.append(layer_cache)
         a = causal_attention(q, k, v, 1.0 / np.sqrt(cfg.head_dim)).reshape(S, -1)
         x = _mlp_tail(x, a, lw, cfg)
-    logits = linear(rms_norm(x, weights.final_norm, cfg.rms_eps), weights.lm_head)
-    return logits, cache, raw
+    out = linear(rms_norm(x, weights.final_norm, cfg.rms_eps), weights.lm_head) if logits else None
+    return out, cache, raw
+
+
+_last_values: dict = {}   # layer -> unquantised value [kv_heads, d] of the last decode step
 
 
 def decode_step(cfg, weights, token: int, cache: SeqCache, v_scale: np.ndarray, exact: bool = False) -> np.ndarray:
@@ -122,6 +125,7 @@ def decode_step(cfg, weights, token: int, cache: SeqCache, v_scale: np.ndarray, 
     for l in range(cfg.n_layers):
         lw = weights.layer(l)
         q, k, v = _qkv(x, lw, cfg, np.array([p]))  # q [1, heads, d]
+        _last_values[l] = v[0]
         _store(cache.layers[l], k, v, v_scale[l], exact)
         if exact:
             K = np.stack([e[0] for e in cache.layers[l]])   # [p + 1, kv_heads, d]

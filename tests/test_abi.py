@@ -119,6 +119,9 @@ def test_other_entry_points_reject_bad_arguments():
     assert app(batch=-1) == 2
     assert app(k_pool=0x604) == 6
     assert app(batch=0) == 0               # nothing to write, nothing enqueued
+    assert L.phi_prefill_fill_k16v8(None, 0x100, 1, 1, 0x200, None, 0x300, 1 << 20, None) == 1
+    assert L.phi_decode_step_k16v8(None, 0x100, 0x200, 1, 1, None, 0x300, 0x400, 1 << 20, None) == 1
+    assert L.phi_decode_workspace_bytes(None, 1, 16) == 0
 
 
 def test_no_packed_fp32_instructions_in_device_code(tmp_path):
