@@ -223,11 +223,15 @@ def main():
     out = {"metric": "Phi-3-mini-shape f16 prefill tokens/s, % MFMA peak; logit cosine vs oracle",
            "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32" if cfg.wtype == "f32" else "f16",
+           "data": "synthetic",
            "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq, "layers": cfg.n_layers,
                       "hidden": cfg.hidden, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                       "intermediate": cfg.intermediate, "vocab": cfg.vocab,
-                      "weights": "random N(0,0.02) float16, seed 1", "ids": "uniform, seed 2"},
+                      "weights": {"f32": "random N(0,0.02) float32, seed 1", "f16": "random N(0,0.02) float16, seed 1",
+                                  "i8": "int8 per-row codes + float16 scales of random N(0,0.02) float16, seed 1"}[
+                          cfg.wtype],
+                      "ids": "uniform, seed 2"},
            "roofline": roof,
            "model_mfma_frac": round(flops / (wall / args.steps) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
            "event_ms_per_step": round(e0.elapsed_time(e1) / args.steps, 4),

@@ -64,10 +64,11 @@ typedef enum phi_wtype { PHI_WT_F32 = 0, PHI_WT_F16 = 1, PHI_WT_I8 = 2 } phi_wty
 
 typedef struct phi_config {
   int32_t n_layers;
-  int32_t hidden;       /* H; multiple of 64, at most 4096                    */
+  int32_t hidden;       /* H; multiple of 64, at most 8192                    */
   int32_t n_heads;      /* query heads                                        */
   int32_t n_kv_heads;   /* divides n_heads (n_kv_heads == n_heads: MHA)       */
-  int32_t head_dim;     /* 96 ([P1] section 2)                                */
+  int32_t head_dim;     /* 96 ([P1] section 2); 64 or 128 on the binary16 and
+                           int8 paths (other dense families, [P3]'s Phi-4)   */
   int32_t intermediate; /* I; multiple of 128                                 */
   int32_t vocab;        /* V; multiple of 4                                   */
   int32_t max_pos;      /* longest sequence; at most 4096 ([P1] section 4)   */
@@ -94,13 +95,18 @@ typedef struct phi_layer_weights {
   const void* ln2;
   phi_linear gate_up;
   phi_linear down;
+  const void* qkv_bias; /* optional [(n_heads + 2 n_kv_heads) head_dim] binary16
+                           added to the fused QKV product before RoPE
+                           (Qwen2-style families, [P2] section 3); NULL: none.
+                           Not on the float32 path.                          */
 } phi_layer_weights;
 
 typedef struct phi_weights {
   const void* embed;                /* [V][H]                                  */
   const phi_layer_weights* layers;  /* host array of n_layers entries          */
   const void* final_norm;           /* [H]                                     */
-  phi_linear lm_head;               /* [V][H], untied from embed ([P1] sec. 2) */
+  phi_linear lm_head;               /* [V][H], untied from embed ([P1] sec. 2);
+                                       a tied model passes embed here        */
 } phi_weights;
 
 typedef struct phi_model phi_model; /* opaque host object */

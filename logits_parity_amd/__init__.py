@@ -52,7 +52,7 @@ class phi_kv_cache(ctypes.Structure):
 
 class phi_layer_weights(ctypes.Structure):
     _fields_ = [("ln1", ctypes.c_void_p), ("qkv", phi_linear), ("o", phi_linear), ("ln2", ctypes.c_void_p),
-                ("gate_up", phi_linear), ("down", phi_linear)]
+                ("gate_up", phi_linear), ("down", phi_linear), ("qkv_bias", ctypes.c_void_p)]
 
 
 class phi_weights(ctypes.Structure):
@@ -143,7 +143,7 @@ class Model:
         layers = (phi_layer_weights * cfg.n_layers)()
         for i, lw in enumerate(weights["layers"]):
             layers[i] = phi_layer_weights(_ptr(lw["ln1"]), _lin(lw["qkv"]), _lin(lw["o"]), _ptr(lw["ln2"]),
-                                          _lin(lw["gate_up"]), _lin(lw["down"]))
+                                          _lin(lw["gate_up"]), _lin(lw["down"]), _ptr(lw.get("qkv_bias")))
         w = phi_weights(_ptr(weights["embed"]), layers, _ptr(weights["final_norm"]), _lin(weights["lm_head"]))
         nbytes = lib().phi_state_bytes(ctypes.byref(self._c))
         dev = weights["embed"].device

@@ -54,7 +54,8 @@ using CfgS = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64
 using CfgQL = TileCfg<256, 192, 2, 2>;  // wave tile 128 x 96 (one head per wave)
 using CfgQS = TileCfg<128, 192, 2, 2>;  // wave tile 64 x 96
 using CfgQ128 = TileCfg<128, 256, 2, 2>;  // wave tile 64 x 128 (one 128-wide head per wave)
-enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128 };
+using CfgQ64 = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64 (one 64-wide head per wave)
+enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64 };
 
 struct GemmPlan {
   int cfg, tiles_m, tiles_n, splits, kpt;
@@ -69,6 +70,7 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
     case C_S: bm = 128; bn = 128; break;
     case C_QL: bm = 256; bn = 192; break;
     case C_Q128: bm = 128; bn = 256; break;
+    case C_Q64: bm = 128; bn = 128; break;
     default: bm = 128; bn = 192; break;
   }
 }
@@ -80,7 +82,7 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 // next to its 256 accumulators, so they take the 256 x 128 tile instead.
 GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   GemmPlan p{};
-  if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (M >= 1024 ? C_QL : C_QS);
+  if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
   else if (epi == EPI_SILU) p.cfg = (M >= 1024 && !w8) ? C_L : C_M;
   else if (epi == EPI_F32) p.cfg = w8 ? C_M : C_L;
   else p.cfg = M >= 2048 ? C_M : C_S;
@@ -120,6 +122,7 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
   if constexpr (EPI == EPI_QKV) {
     if (cfg == C_QL) launch_mfma<CfgQL, W8, EPI>(a, st);
     else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st);
+    else if (cfg == C_Q64) launch_mfma<CfgQ64, W8, EPI>(a, st);
     else launch_mfma<CfgQS, W8, EPI>(a, st);
   } else if constexpr (EPI == EPI_SILU) {
     if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
@@ -170,9 +173,9 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   return p;
 }
 
-// head_dim 128 runs on the MFMA paths only (binary16 and int8 weights).
+// head_dim 64 and 128 run on the MFMA paths only (binary16 and int8 weights).
 bool check_config(const phi_config* c) {
-  const bool hd_ok = c->head_dim == 96 || (c->head_dim == 128 && c->wtype != PHI_WT_F32);
+  const bool hd_ok = c->head_dim == 96 || ((c->head_dim == 64 || c->head_dim == 128) && c->wtype != PHI_WT_F32);
   return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && hd_ok &&
          c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
          (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 128 && c->intermediate % 128 == 0 &&
@@ -226,6 +229,7 @@ phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
   }
   const dim3 grid((a.S + 31) / 32, a.nh, batch);
   if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<128, 4>), grid, dim3(256), 0, st, a);
+  else if (hd == 64) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<64, 4>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<96, 4>), grid, dim3(256), 0, st, a);
   return launched();
 }
@@ -341,6 +345,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.q = const_cast<void*>(aa.q);
     g.k = const_cast<void*>(aa.k);
     g.vt = const_cast<void*>(aa.vt);
+    g.bias = reinterpret_cast<const f16*>(L.qkv_bias);
     tm.begin(PHI_PROF_QKV);
     s = gemm<EPI_QKV>(wt, g, p.qkv, st);
     if (!s && cache) s = kv_fill(cache, l, aa.k, aa.vt, batch, seq, p.s_pad, c.n_kv_heads, st);
@@ -594,6 +599,7 @@ phi_status decode_step(const phi_model* m, const int32_t* ids, const int32_t* po
     g.q = q;
     g.k = k;
     g.vt = v;
+    g.bias = reinterpret_cast<const f16*>(L.qkv_bias);
     if ((s = gemm<EPI_QKV>(wt, g, p.qkv, st))) return s;
     const float* vs = cache->v_scale + (size_t)l * c.n_kv_heads;
     if ((s = kv_append(k, v, vs, cache->block_table, positions, B, c.n_kv_heads, cache->n_pages,
@@ -707,6 +713,8 @@ phi_status phi_load_fused(const phi_config* cfg, const phi_weights* w, void* sta
     const phi_layer_weights& L = w->layers[l];
     if (!L.ln1 || !L.ln2 || !lin_ok(L.qkv) || !lin_ok(L.o) || !lin_ok(L.gate_up) || !lin_ok(L.down))
       return PHI_E_NULL;
+    if (L.qkv_bias && cfg->wtype == PHI_WT_F32) return PHI_E_DTYPE;  // the float32 path has no bias
+    if (!aligned16(L.qkv_bias)) return PHI_E_ALIGN;
     const void* ps[] = {L.ln1, L.ln2, L.qkv.w, L.qkv.scale, L.o.w, L.o.scale,
                         L.gate_up.w, L.gate_up.scale, L.down.w, L.down.scale};
     for (const void* p : ps)
@@ -847,7 +855,7 @@ phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, 
                                  void* stream) {
   if (!q || !k || !vt || !out) return PHI_E_NULL;
   if (batch < 1 || seq < 1 || n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads ||
-      (head_dim != 96 && !(head_dim == 128 && !act_f32)))
+      (head_dim != 96 && !((head_dim == 64 || head_dim == 128) && !act_f32)))
     return PHI_E_SHAPE;
   if (seq > kMaxPos) return PHI_E_RANGE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out)) return PHI_E_ALIGN;

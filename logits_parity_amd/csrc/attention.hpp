@@ -1,5 +1,5 @@
 // Causal softmax attention for the prefill, head_dim 96 (binary16 and float32)
-// or 128 (binary16).
+// or 64 and 128 (binary16).
 //
 // binary16 path (split keys, MFMA): a workgroup owns 32 queries of one
 // (sequence, head) and its 4 waves take the 64-key blocks that reach those
@@ -13,8 +13,8 @@
 // each lane holds one query's column: the running max, sum and output rescale
 // are per-lane scalars, and only the max needs one exchange (lanes l, l + 32).
 // The output is accumulated transposed too, O^T += V^T P^T, with P^T taken
-// straight from the score registers.  A key block is 64 keys at head_dim 96
-// and 32 at head_dim 128 (register budget).  Key rows enter the score MFMA with bits
+// straight from the score registers.  A key block is 64 keys at head_dim 64
+// and 96, and 32 at head_dim 128 (register budget).  Key rows enter the score MFMA with bits
 // 2 and 3 of their index swapped; then the 8 score registers of each half of
 // a lane hold 8 consecutive keys, and the matching V^T operand of the output
 // MFMA is one 16-byte load.  Operands come from bounds-checked buffer loads
@@ -45,8 +45,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, in
 
 template <int D, int NKV>
 __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnArgs a) {
-  static_assert(D == 96 || D == 128, "head_dim");
-  constexpr int HB = D == 96 ? 2 : 1;       // 32-key halves per key block (register budget)
+  static_assert(D == 64 || D == 96 || D == 128, "head_dim");
+  constexpr int HB = D == 128 ? 1 : 2;      // 32-key halves per key block (register budget)
   constexpr int KB = 32 * HB, OLD = D + 4, KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) float sO[NKV][32 * OLD];  // per wave: O[query][d], unnormalised
   __shared__ float sM[NKV][32], sL[NKV][32];

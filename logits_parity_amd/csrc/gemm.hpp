@@ -31,7 +31,8 @@
 //  EPI_SILU     fused gate/up: the tile reads weight rows in 32-row blocks
 //               alternating gate, up for the same outputs, so a lane holds
 //               gate and up of one output: act = silu(gate) * up
-//  EPI_QKV      fused Q/K/V, one head (96 or 128 wide) per wave: the head's
+//  EPI_QKV      fused Q/K/V, one head (64, 96 or 128 wide) per wave, plus an
+//               optional per-row bias before RoPE: the head's
 //               weight rows are read in an order that puts RoPE pairs
 //               (d, d + HD / 2) in one lane (HD = 128: blocks 0..31 | 64..95 |
 //               32..63 | 96..127) or, for the third block of HD = 96 (rows
@@ -67,6 +68,7 @@ struct GemmArgs {
   const float* rope_cos;  // [max_pos][hd/2]
   const float* rope_sin;
   const int32_t* pos;     // EPI_QKV: RoPE position of each token row (nullptr: row mod S)
+  const f16* bias;        // EPI_QKV: optional per-row bias of the fused product (nullptr: none)
   int max_pos;
   int S, s_pad, nh, nkv, hd;
 };
@@ -77,9 +79,11 @@ struct GemmArgs {
 //   HD = 96:  blocks hold d = 0..31 | 48..79 | 32..47, 80..95 (the third
 //             block's partners sit in lanes l and l ^ 16)
 //   HD = 128: blocks hold d = 0..31 | 64..95 | 32..63 | 96..127
+//   HD = 64:  blocks hold d = 0..31 | 32..63 (natural order)
 template <int HD>
 __device__ __forceinline__ int qkv_head_row(int j) {
-  if constexpr (HD == 96) return j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
+  if constexpr (HD == 64) return j;  // blocks 0..31 | 32..63 already pair up
+  else if constexpr (HD == 96) return j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
   else return j < 32 ? j : (j < 64 ? j + 32 : (j < 96 ? j - 32 : j));
 }
 
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   static_assert(LPW * NW == INS_A + INS_W, "stage split");
   static_assert(!W8 || CB8 * NT == BN * 4, "int8 split");
   static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
-  static_assert(EPI != EPI_QKV || WN == 96 || WN == 128, "QKV: one head (96 or 128 wide) per wave");
+  static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
   constexpr int HD = EPI == EPI_QKV ? WN : 96;
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
 
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) dd[j] = qkv_head_row<HD>(j * 32 + col_l);
     const int fA = col_l;                                            // blocks 0, 1
-    const int fB = HD == 96 ? 32 + (col_l & 15) : 32 + col_l;        // block 2 (and 3)
+    const int fB = HD == 96 ? 32 + (col_l & 15) : (HD == 128 ? 32 + col_l : 0);  // block 2 (and 3)
     const int mw0 = m0 + wm * WM;      // first token row of this wave
     // rotation factors of the lane's rows: all loads in flight at once, before
     // the barrier.  Position = pos[row] when given, else row mod S.
@@ -369,10 +373,17 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
           const size_t t = (size_t)sp * HALF;
           cA[i][v] = a.rope_cos[t + fA];
           sA[i][v] = a.rope_sin[t + fA];
-          cB[i][v] = a.rope_cos[t + fB];
-          sB[i][v] = a.rope_sin[t + fB];
+          if constexpr (HD > 64) {
+            cB[i][v] = a.rope_cos[t + fB];
+            sB[i][v] = a.rope_sin[t + fB];
+          }
         }
     }
+    // per-row bias of the fused product (one value per lane and block)
+    float bj[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bj[j] = (a.bias && col0 < a.N) ? (float)a.bias[w_row_mfma<EPI, BN, HD>(a, tn, wn * WN + j * 32 + col_l)] : 0.f;
     __syncthreads();                      // every wave is done with the k-stages
     if (col0 >= a.N) return;
     f16* tile = smem + wave * REG;
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
         for (int v = 0; v < 16; ++v) {
           const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) tile[dd[j] * VLD + r] = (f16)(acc[i][j][v] * sc[j]);
+          for (int j = 0; j < TN; ++j) tile[dd[j] * VLD + r] = (f16)(acc[i][j][v] * sc[j] + bj[j]);
         }
     } else {
 #pragma unroll
@@ -391,15 +402,15 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
-          const float y0 = acc[i][0][v] * sc[0], y1 = acc[i][1][v] * sc[1];
+          const float y0 = acc[i][0][v] * sc[0] + bj[0], y1 = acc[i][1][v] * sc[1] + bj[1];
           tile[r * QLD + dd[0]] = (f16)(y0 * cA[i][v] - y1 * sA[i][v]);
           tile[r * QLD + dd[1]] = (f16)(y1 * cA[i][v] + y0 * sA[i][v]);
           if constexpr (HD == 96) {
-            const float y2 = acc[i][2][v] * sc[2];
+            const float y2 = acc[i][2][v] * sc[2] + bj[2];
             const float y2p = __shfl_xor(y2, 16);  // partner of the third block
             tile[r * QLD + dd[2]] = (f16)(col_l < 16 ? y2 * cB[i][v] - y2p * sB[i][v] : y2 * cB[i][v] + y2p * sB[i][v]);
-          } else {
-            const float y2 = acc[i][2][v] * sc[2], y3 = acc[i][3][v] * sc[3];
+          } else if constexpr (HD == 128) {
+            const float y2 = acc[i][2][v] * sc[2] + bj[2], y3 = acc[i][3][v] * sc[3] + bj[3];
             tile[r * QLD + dd[2]] = (f16)(y2 * cB[i][v] - y3 * sB[i][v]);
             tile[r * QLD + dd[3]] = (f16)(y3 * cB[i][v] + y2 * sB[i][v]);
           }

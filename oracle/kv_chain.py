@@ -72,6 +72,8 @@ def _qkv(x, lw, cfg, positions):
     T = x.shape[0]
     xn = rms_norm(x, lw["ln1"], cfg.rms_eps)
     qkv = linear(xn, lw["qkv"])
+    if "qkv_bias" in lw:
+        qkv = qkv + widen(lw["qkv_bias"])
     q = qkv[:, : nh * hd].reshape(T, nh, hd)
     k = qkv[:, nh * hd : (nh + nkv) * hd].reshape(T, nkv, hd)
     v = qkv[:, (nh + nkv) * hd :].reshape(T, nkv, hd)

@@ -84,11 +84,15 @@ def decoder_layer(x: np.ndarray, lw: dict, cfg, positions: np.ndarray) -> np.nda
 
     Fused Q/K/V: one product with the concatenated [Wq; Wk; Wv], rows split in
     that order; fused gate/up: one product with [Wg; Wu], gate rows first
-    (P1 section 1: the fused tensors are used as single tensors)."""
+    (P1 section 1: the fused tensors are used as single tensors).  An optional
+    qkv_bias is added to that product before RoPE: the Qwen2 family of the
+    parity harness page (section 3) carries one, Phi-3 does not."""
     nh, nkv, hd, I = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate
     S = x.shape[0]
     xn = rms_norm(x, lw["ln1"], cfg.rms_eps)
     qkv = linear(xn, lw["qkv"])
+    if "qkv_bias" in lw:
+        qkv = qkv + widen(lw["qkv_bias"])
     q = qkv[:, : nh * hd].reshape(S, nh, hd)
     k = qkv[:, nh * hd : (nh + nkv) * hd].reshape(S, nkv, hd)
     v = qkv[:, (nh + nkv) * hd :].reshape(S, nkv, hd)

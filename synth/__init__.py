@@ -156,6 +156,8 @@ class PhiConfig:
     rope_theta: float = 10000.0
     wtype: str = "f16"          # "f32", "f16" or "i8" (per-row int8 + f16 scale)
     norm_gain: str = "normal"   # "normal": N(0, 0.02) like every weight; "ones": diagnostic
+    qkv_bias: bool = False      # a bias on the fused QKV product (Qwen2-style)
+    tie_embeddings: bool = False  # lm_head is the embedding matrix
 
     @property
     def qkv_rows(self) -> int:
@@ -183,6 +185,15 @@ TINY_GQA128 = PhiConfig("tiny_gqa128", n_layers=2, hidden=512, n_heads=4, n_kv_h
                         intermediate=1024, vocab=4096, rope_theta=250000.0, wtype="f16")
 PHI4_1L = PhiConfig("phi4_1l", n_layers=1, hidden=5120, n_heads=40, n_kv_heads=10, head_dim=128,
                     intermediate=17920, vocab=100352, rope_theta=250000.0, wtype="f16")
+# the two other dense families of the parity harness page, at their public
+# shapes: Qwen2.5-0.5B-style (GQA 14/2 at head_dim 64, QKV bias, tied
+# embeddings) and SmolLM2-360M-style (GQA 15/5 at head_dim 64, tied)
+QWEN25_05B = PhiConfig("qwen25_05b", n_layers=24, hidden=896, n_heads=14, n_kv_heads=2, head_dim=64,
+                       intermediate=4864, vocab=151936, rms_eps=1e-6, rope_theta=1000000.0, wtype="f16",
+                       qkv_bias=True, tie_embeddings=True)
+SMOLLM2_360M = PhiConfig("smollm2_360m", n_layers=32, hidden=960, n_heads=15, n_kv_heads=5, head_dim=64,
+                         intermediate=2560, vocab=49152, rms_eps=1e-5, rope_theta=100000.0, wtype="f16",
+                         tie_embeddings=True)
 
 
 @dataclass(frozen=True)
@@ -264,6 +275,9 @@ def layer_weights(cfg: PhiConfig, layer: int, seed: int = WEIGHT_SEED) -> dict:
     out = {"ln1": _gain(cfg, p + "ln1", seed), "ln2": _gain(cfg, p + "ln2", seed)}
     for nm, shape in cfg.linear_shapes().items():
         out[nm] = _linear(cfg, p + nm, shape, seed)
+    if cfg.qkv_bias:
+        # activation type (float16 also for int8 weights)
+        out["qkv_bias"] = normal(seed, p + "qkv_bias", (cfg.qkv_rows,), WEIGHT_STD, cfg.act_dtype)
     return out
 
 
@@ -276,6 +290,9 @@ def final_norm_weight(cfg: PhiConfig, seed: int = WEIGHT_SEED):
 
 
 def lm_head_weight(cfg: PhiConfig, seed: int = WEIGHT_SEED):
+    if cfg.tie_embeddings:
+        e = embed_weight(cfg, seed)
+        return quantize_rows_i8(e) if cfg.wtype == "i8" else e
     return _linear(cfg, "lm_head", (cfg.vocab, cfg.hidden), seed)
 
 
@@ -314,6 +331,8 @@ class WeightSet:
 
     @property
     def lm_head(self):
+        if self.cfg.tie_embeddings and self.cfg.wtype != "i8":
+            return self.embed          # the same array: a tied model shares the tensor
         if self._lm is None:
             self._lm = lm_head_weight(self.cfg, self.seed)
         return self._lm
@@ -332,8 +351,9 @@ class WeightSet:
         feed(self.embed)
         for l in range(self.cfg.n_layers):
             w = self.layer(l)
-            for nm in ("ln1", "qkv", "o", "ln2", "gate_up", "down"):
-                feed(w[nm])
+            for nm in ("ln1", "qkv", "o", "ln2", "gate_up", "down", "qkv_bias"):
+                if nm in w:
+                    feed(w[nm])
         feed(self.final_norm)
         feed(self.lm_head)
         return h.hexdigest()
