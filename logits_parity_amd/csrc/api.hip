@@ -77,14 +77,14 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 
 // Tile shape per GEMM role and token count: large wave tiles keep LDS traffic
 // per MFMA low; at small M the residual GEMMs (N = hidden) have too few tiles
-// for 256 CUs, so K is split until every CU has work.
-// int8 weights stage through VGPRs, which the 256 x 256 tile cannot afford
-// next to its 256 accumulators, so they take the 256 x 128 tile instead.
+// for 256 CUs, so K is split until every CU has work.  int8 and binary16
+// weights share the plans (both go global -> LDS by DMA).
 GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   GemmPlan p{};
+  (void)w8;
   if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
-  else if (epi == EPI_SILU) p.cfg = (M >= 1024 && !w8) ? C_L : C_M;
-  else if (epi == EPI_F32) p.cfg = w8 ? C_M : C_L;
+  else if (epi == EPI_SILU) p.cfg = M >= 1024 ? C_L : C_M;
+  else if (epi == EPI_F32) p.cfg = C_L;
   else p.cfg = M >= 2048 ? C_M : C_S;
   int bm, bn;
   cfg_dims(p.cfg, bm, bn);
@@ -101,12 +101,12 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
 
 // LDS stages of a tile.  Tiles whose two stages leave room for a second
 // workgroup per CU keep 2 (the other workgroup covers the load latency);
-// larger tiles take 3 when they fit in 152 KB.  int8 weights, which stage
-// through VGPRs one k-step ahead, use 2.
+// larger tiles take 3 when they fit in 152 KB.  int8 weights take half the
+// bytes of binary16 ones.
 template <class C, bool W8>
 constexpr int gemm_stages() {
-  constexpr int stage_bytes = (C::BM + C::BN) * 64 * 2;
-  if (W8 || 2 * stage_bytes <= 64 * 1024) return 2;
+  constexpr int stage_bytes = C::BM * 64 * 2 + C::BN * 64 * (W8 ? 1 : 2);
+  if (2 * stage_bytes <= 64 * 1024) return 2;
   return 3 * stage_bytes <= 152 * 1024 ? 3 : 2;
 }
 
@@ -125,12 +125,10 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
     else if (cfg == C_Q64) launch_mfma<CfgQ64, W8, EPI>(a, st);
     else launch_mfma<CfgQS, W8, EPI>(a, st);
   } else if constexpr (EPI == EPI_SILU) {
-    if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
-    else if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st);
+    if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st);
     else launch_mfma<CfgM, W8, EPI>(a, st);
   } else if constexpr (EPI == EPI_F32) {
-    if constexpr (W8) launch_mfma<CfgM, W8, EPI>(a, st);
-    else launch_mfma<CfgL, W8, EPI>(a, st);
+    launch_mfma<CfgL, W8, EPI>(a, st);
   } else {
     if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st);
     else launch_mfma<CfgS, W8, EPI>(a, st);
@@ -171,6 +169,13 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.off_part = take(max_split > 1 ? (size_t)max_split * T * H * 4 : 0);
   p.total = o;
   return p;
+}
+
+// Token rows times the widest GEMM operand row (hidden, intermediate or
+// attention width) stay within int32 element offsets.
+bool rows_fit(const phi_config& c, long long rows) {
+  const long long w = std::max({(long long)c.hidden, (long long)c.intermediate, (long long)c.n_heads * c.head_dim});
+  return rows >= 1 && rows * w < (1ll << 31) && rows * c.vocab < (1ll << 40);
 }
 
 // head_dim 64 and 128 run on the MFMA paths only (binary16 and int8 weights).
@@ -761,7 +766,7 @@ phi_status phi_prefill_logits(const phi_model* m, const int32_t* ids, int32_t ba
   if (!m || !ids || !logits || !workspace) return PHI_E_NULL;
   if (batch < 1 || seq < 1) return PHI_E_SHAPE;
   if (seq > m->cfg.max_pos) return PHI_E_RANGE;
-  if ((long long)batch * seq > (1 << 24)) return PHI_E_SHAPE;
+  if (!rows_fit(m->cfg, (long long)batch * seq)) return PHI_E_SHAPE;
   if (workspace_bytes < plan_prefill(m->cfg, batch, seq).total) return PHI_E_WORKSPACE;
   if (!aligned16(ids) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
   hipStream_t st = as_stream(stream);
@@ -922,7 +927,7 @@ phi_status phi_prefill_fill_k16v8(const phi_model* m, const int32_t* ids, int32_
   if (s) return s;
   if (batch < 1 || seq < 1) return PHI_E_SHAPE;
   if (seq > m->cfg.max_pos || seq > cache->max_pages * 16) return PHI_E_RANGE;
-  if ((long long)batch * seq > (1 << 24)) return PHI_E_SHAPE;
+  if (!rows_fit(m->cfg, (long long)batch * seq)) return PHI_E_SHAPE;
   if (workspace_bytes < plan_prefill(m->cfg, batch, seq).total) return PHI_E_WORKSPACE;
   if (!aligned16(ids) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
   const PhiProfile& pr = m->prof;
@@ -941,7 +946,7 @@ phi_status phi_decode_step_k16v8(const phi_model* m, const int32_t* ids, const i
   if (!m || !ids || !positions || !logits || !workspace || !cache) return PHI_E_NULL;
   phi_status s = check_cache(m, cache);
   if (s) return s;
-  if (batch < 1 || batch > (1 << 16)) return PHI_E_SHAPE;
+  if (batch < 1 || batch > (1 << 16) || !rows_fit(m->cfg, batch)) return PHI_E_SHAPE;
   if (max_ctx < 1 || max_ctx > cache->max_pages * 16 || max_ctx > m->cfg.max_pos) return PHI_E_RANGE;
   if (workspace_bytes < plan_decode_step(m->cfg, batch, max_ctx).total) return PHI_E_WORKSPACE;
   if (!aligned16(ids) || !aligned16(positions) || !aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;

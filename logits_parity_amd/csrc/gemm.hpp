@@ -5,16 +5,17 @@
 //    v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators.
 //  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
 //    them in flight while one is consumed, so the DMA of a k-step has NS - 1
-//    k-steps of MFMA work to arrive.  binary16 operands go global -> LDS
-//    directly (global_load_lds_dwordx4, no VGPR staging): one wave
-//    instruction fills 1 KB = 8 rows of 128 B.  int8 weights are loaded
-//    into VGPRs, widened exactly to binary16 (|q| <= 127) and written to LDS
-//    one k-step ahead (NS = 2); their per-row scale multiplies the fp32
-//    accumulator (it factors out of the K sum).
+//    k-steps of MFMA work to arrive.  Operands go global -> LDS directly
+//    (global_load_lds_dwordx4, no VGPR staging): one wave instruction fills
+//    1 KB = 8 binary16 rows of 128 B, or 16 int8 weight rows of 64 B.  int8
+//    codes are widened exactly to binary16 (|q| <= 127) as their fragments
+//    are read from LDS; the per-row scale multiplies the fp32 accumulator (it
+//    factors out of the K sum).
 //  - Rows are stored with an XOR swizzle of their 16-byte chunks,
 //    chunk' = chunk ^ ((row >> 1) & 7): 16 lanes reading 16 consecutive rows
 //    at one logical chunk touch 16 distinct 16-byte bank groups of the
-//    256-byte LDS bank row, so fragment reads are conflict free.
+//    256-byte LDS bank row, so fragment reads are conflict free (int8 rows:
+//    chunk' = chunk ^ ((row >> 1) & 3) over their four chunks).
 //  - Each k-step's fragment reads for step s+1 are issued before the MFMAs of
 //    step s (scheduling barriers keep the compiler from re-serialising them).
 //  - Split-K: a launch may cut K into `splits` ranges; each writes an fp32
@@ -120,12 +121,20 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
+// Eight int8 codes (two dwords) -> binary16, exactly: with the sign bit
+// flipped a code q is the byte u = q + 128, and the binary16 with high byte
+// 0x64 and low byte u is 1024 + u; subtracting 1152 leaves q.
 __device__ __forceinline__ f16x8 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  const uint32_t x0 = lo ^ 0x80808080u, x1 = hi ^ 0x80808080u;
+  const uint32_t k = 0x64646464u;
   f16x8 o;
+  const uint32_t w[4] = {__builtin_amdgcn_perm(k, x0, 0x04010400u), __builtin_amdgcn_perm(k, x0, 0x04030402u),
+                         __builtin_amdgcn_perm(k, x1, 0x04010400u), __builtin_amdgcn_perm(k, x1, 0x04030402u)};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    o[e] = (f16)(float)(int8_t)(lo >> (8 * e));
-    o[4 + e] = (f16)(float)(int8_t)(hi >> (8 * e));
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]) - f16x2{(f16)1152.f, (f16)1152.f};
+    o[2 * i] = h[0];
+    o[2 * i + 1] = h[1];
   }
   return o;
 }
@@ -143,20 +152,26 @@ template <class C, bool W8, int EPI, int NS>
 __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
   constexpr int NT = C::NT, NW = C::NW, BK = 64;
-  static_assert(NS >= 2 && NS <= 4 && (!W8 || NS == 2), "stages: int8 weights stage through VGPRs, 2 stages");
-  constexpr int STAGE = (BM + BN) * BK;              // f16 elements per LDS stage
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  // An LDS stage holds A [BM][64] binary16 (128-byte rows, eight 16-byte
+  // chunks) then W [BN][64]: binary16 (128-byte rows), or int8 codes
+  // (64-byte rows, four 16-byte chunks) widened to binary16 when fragments
+  // are read.  Both go global -> LDS by DMA, 1 KB per wave instruction.
+  constexpr int WB = W8 ? 1 : 2;                     // bytes per weight element
+  constexpr int STAGE = (BM * BK * 2 + BN * BK * WB) / 2;  // f16 elements per LDS stage
   constexpr int INS_A = BM * 8 / 64;                 // 1 KB DMA instructions for A per stage
-  constexpr int INS_W = W8 ? 0 : BN * 8 / 64;
+  constexpr int INS_W = BN * BK * WB / 1024;
   constexpr int LPW = (INS_A + INS_W) / NW;          // DMA instructions per wave per stage
-  constexpr int CB8 = W8 ? BN * 4 / NT : 0;          // int8 16-byte chunks per thread per stage
   static_assert(LPW * NW == INS_A + INS_W, "stage split");
-  static_assert(!W8 || CB8 * NT == BN * 4, "int8 split");
   static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
   static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
   constexpr int HD = EPI == EPI_QKV ? WN : 96;
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
 
-  __shared__ __attribute__((aligned(1024))) f16 smem[NS * STAGE];
+  // the QKV epilogue stages each wave's head tile in the same LDS
+  constexpr int QKV_REG = EPI == EPI_QKV ? ((WM * (HD + 8) > HD * (WM + 8)) ? WM * (HD + 8) : HD * (WM + 8)) : 0;
+  constexpr int SMEM = NS * STAGE > NW * QKV_REG ? NS * STAGE : NW * QKV_REG;
+  __shared__ __attribute__((aligned(1024))) f16 smem[SMEM];
 
   const int n_units = a.tiles_m * a.tiles_n * a.splits;
   const int unit = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -170,7 +185,10 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   const int K = a.K;
   const f16* A = reinterpret_cast<const f16*>(a.A);
 
-  // DMA sources: instruction j = wave + NW * t fills LDS slots [64 j, 64 j + 64)
+  // DMA sources (element offsets in the operand's own type; the host keeps
+  // rows x K within int32): instruction j = wave + NW * t fills LDS bytes
+  // [1024 j, 1024 j + 1024) of the stage; the lane's 16-byte slot holds a
+  // swizzled chunk of one row
   int src_off[LPW > 0 ? LPW : 1];
   bool src_is_w[LPW > 0 ? LPW : 1];
 #pragma unroll
@@ -178,43 +196,31 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     const int j = wave + NW * t;
     const int s = j * 64 + lane;
     const bool is_w = j >= INS_A;
-    const int r = (is_w ? s - INS_A * 64 : s) >> 3, p = s & 7;
-    const int c = p ^ ((r >> 1) & 7);
-    int row;
-    if (is_w) row = w_row_mfma<EPI, BN, HD>(a, tn, r);
-    else row = m0 + r < a.M ? m0 + r : a.M - 1;
-    src_off[t] = row * K + c * 8;
+    if (!is_w) {
+      const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+      src_off[t] = (m0 + r < a.M ? m0 + r : a.M - 1) * K + c * 8;
+    } else if constexpr (W8) {
+      const int sw = s - INS_A * 64, r = sw >> 2, c = (sw & 3) ^ ((r >> 1) & 3);
+      src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 16;
+    } else {
+      const int sw = s - INS_A * 64, r = sw >> 3, c = (sw & 7) ^ ((r >> 1) & 7);
+      src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 8;
+    }
     src_is_w[t] = is_w;
   }
   const f16* Wf = reinterpret_cast<const f16*>(a.W);
   const int8_t* W8p = reinterpret_cast<const int8_t*>(a.W);
-  int w8_off[CB8 > 0 ? CB8 : 1];
-#pragma unroll
-  for (int i = 0; i < CB8; ++i) {
-    const int q = tid + i * NT, r = q >> 2, c = q & 3;
-    w8_off[i] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 16;
-  }
-  i32x4 rw8[CB8 > 0 ? CB8 : 1];
 
   auto issue = [&](int kt, f16* st) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
       const int j = wave + NW * t;
-      const f16* g = (src_is_w[t] ? Wf : A) + src_off[t] + k0;
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)(st + j * 512), 16, 0, 0);
-    }
-    if constexpr (W8) {
-#pragma unroll
-      for (int i = 0; i < CB8; ++i) rw8[i] = *reinterpret_cast<const i32x4*>(W8p + w8_off[i] + k0);
-    }
-  };
-  auto store_w8 = [&](f16* st) {
-#pragma unroll
-    for (int i = 0; i < CB8; ++i) {
-      const int q = tid + i * NT, r = q >> 2, c = q & 3;
-      *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c)) = i8x8_to_f16x8(rw8[i][0], rw8[i][1]);
-      *reinterpret_cast<f16x8*>(st + BM * BK + swz(r, 2 * c + 1)) = i8x8_to_f16x8(rw8[i][2], rw8[i][3]);
+      const void* g;
+      if (!src_is_w[t]) g = A + src_off[t] + k0;
+      else if constexpr (W8) g = W8p + src_off[t] + k0;
+      else g = Wf + src_off[t] + k0;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024), 16, 0, 0);
     }
   };
 
@@ -230,9 +236,6 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
     if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
-  if constexpr (W8) {
-    if (kt0 < kt1) store_w8(smem);
-  }
   for (int kt = kt0; kt < kt1; ++kt) {
     const int rel = kt - kt0;
     f16* cur = smem + (rel % NS) * STAGE;
@@ -243,16 +246,23 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     else if (newer == 1) PHI_WAIT_VMCNT(LPW);
     else PHI_WAIT_VMCNT(2 * LPW);
     lds_barrier();
-    const bool more = kt + NS - 1 < kt1;
-    if (more) issue(kt + NS - 1, nxt);
+    if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
     f16x8 af[2][TM], bf[2][TN];
+    const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
     // B fragments first, then A in MFMA order: the first MFMAs of a step
     // wait only for the oldest reads, the last reads overlap with them
     auto ld = [&](int kk, f16x8* fa, f16x8* fb) {
       const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(wn * WN + j * 32 + (lane & 31), c));
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WN + j * 32 + (lane & 31);
+        if constexpr (W8) {
+          const uint2 q = *reinterpret_cast<const uint2*>(curw + r * 64 + 16 * (kk ^ ((r >> 1) & 3)) + 8 * (lane >> 5));
+          fb[j] = i8x8_to_f16x8(q.x, q.y);
+        } else {
+          fb[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, c));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         fa[i] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + i * 32 + (lane & 31), c));
@@ -283,9 +293,6 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
-    }
-    if constexpr (W8) {
-      if (more) store_w8(nxt);
     }
   }
 
@@ -337,8 +344,8 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     constexpr int HALF = HD / 2;
     constexpr int QLD = HD + 8;           // Q/K staging row stride (conflict-free writes)
     constexpr int VLD = WM + 8;           // V^T staging row stride
-    constexpr int REG = (WM * QLD > HD * VLD) ? WM * QLD : HD * VLD;
-    static_assert(NW * REG <= NS * STAGE, "QKV staging fits in the stage buffers");
+    constexpr int REG = QKV_REG;
+    static_assert(REG == ((WM * QLD > HD * VLD) ? WM * QLD : HD * VLD) && NW * REG <= SMEM, "QKV staging");
     const int col0 = tn * BN + wn * HD;   // first fused row of this wave's head
     const int q_end = a.nh * HD, k_end = (a.nh + a.nkv) * HD;
     const bool is_v = col0 >= k_end;
