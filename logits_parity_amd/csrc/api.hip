@@ -226,13 +226,28 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
   return launched();
 }
 
+// Workgroups of the shared-key-block attention at which it beats the split
+// kernel (measured: 448 and more win at head_dim 64 to 128, 256 lose).
+constexpr long kAttnSharedMinWorkgroups = 384;
+
 phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
   a.scale_log2 = kLog2e / sqrtf((float)hd);
   if (f32) {
     hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
     return launched();
   }
-  const dim3 grid((a.S + 31) / 32, a.nh, batch);
+  // Shared key blocks (128 queries per workgroup) once there are enough
+  // workgroups to fill the chip at two per CU; split keys (32 queries per
+  // workgroup, four times the workgroups) below that.
+  const int heads = a.nh * batch;
+  if ((long)heads * ((a.S + 127) / 128) >= kAttnSharedMinWorkgroups) {
+    const dim3 grid(heads, (a.S + 127) / 128);
+    if (hd == 128) hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<128>, grid, dim3(256), 0, st, a);
+    else if (hd == 64) hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<64>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<96>, grid, dim3(256), 0, st, a);
+    return launched();
+  }
+  const dim3 grid(heads, (a.S + 31) / 32);
   if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<128, 4>), grid, dim3(256), 0, st, a);
   else if (hd == 64) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<64, 4>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<96, 4>), grid, dim3(256), 0, st, a);

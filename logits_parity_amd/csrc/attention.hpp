@@ -1,7 +1,12 @@
 // Causal softmax attention for the prefill, head_dim 96 (binary16 and float32)
 // or 64 and 128 (binary16).
 //
-// binary16 path (split keys, MFMA): a workgroup owns 32 queries of one
+// binary16 paths (MFMA).  Two kernels share the score/softmax/output
+// formulation below: the split-key kernel for launches with few workgroups,
+// and the shared-key-block kernel (further down) for long sequences and
+// large batches, where it reads each key block from HBM once per 128 queries.
+//
+// Split keys: a workgroup owns 32 queries of one
 // (sequence, head) and its 4 waves take the 64-key blocks that reach those
 // queries round-robin, each keeping its own online-softmax state; the states
 // are merged by log-sum-exp through LDS at the end.  Small workgroups and
@@ -20,8 +25,11 @@
 // MFMA is one 16-byte load.  Operands come from bounds-checked buffer loads
 // over the (sequence, KV head) slice: key rows past the sequence read as zero,
 // value columns past it are zeroed before use.  Softmax runs in base 2
-// on fp32 scores; P enters the MFMA as binary16.  Query blocks are issued
-// last-first so the longest rows start first.
+// on fp32 scores; P enters the MFMA as binary16.  The grid is (heads x
+// batch, query blocks) with query blocks reversed, so the longest workgroups
+// of every head are dispatched first (a greedy longest-first schedule over
+// the whole grid), and consecutive workgroups, which go to different XCDs,
+// are different heads of the same query block.
 //
 // float32 path: one thread per query, online softmax over keys t <= s.
 #pragma once
@@ -38,9 +46,63 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(D)
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+#ifndef PHI_WAIT_VMCNT
+// s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
+#define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#endif
+// Workgroup barrier that waits for this wave's LDS operations only.
+__device__ __forceinline__ void attn_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Buffer resource over [base, base + bytes): loads outside read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// One key block of the online softmax, in place.  sc holds raw scores
+// q . k of NH 32-key halves (register v of half hb: key 32 hb + 16 (v / 8) +
+// 8 grp + v % 8 of the block); on return it holds P = 2^(c s - m) with the
+// running max m (in log2 units, c = log2(e) / sqrt(D)) and the running sum
+// l updated.  Keys above kmax (relative to the lane's 8 grp offset) are
+// masked when diag is set.  The output accumulators are rescaled only when
+// some lane's max grew (a wave-uniform branch; the factor is exactly 1
+// otherwise).  v_exp_f32 is used directly: arguments below -126 give 0 or a
+// subnormal instead of the exact tiny value, which binary16 P cannot hold.
+template <int NH, int DB>
+__device__ __forceinline__ void softmax_block(f32x16 (&sc)[NH], f32x16 (&o)[DB], float& m_run, float& l_run, float c,
+                                              bool diag, int kmax) {
+  if (diag) {
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sc[hb][v] = 32 * hb + 16 * (v >> 3) + (v & 7) > kmax ? -__builtin_inff() : sc[hb][v];
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[hb][v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx * c);  // finite: every lane has an unmasked key in its first block
+  float psum = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(sc[hb][v], c, -m_new));
+      sc[hb][v] = e;
+      psum += e;
+    }
+  if (__ballot(m_new > m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block (m_run = -inf)
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] *= alpha;
+  }
+  m_run = m_new;
+  l_run += psum;
 }
 
 template <int D, int NKV>
@@ -51,8 +113,10 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
   __shared__ __attribute__((aligned(16))) float sO[NKV][32 * OLD];  // per wave: O[query][d], unnormalised
   __shared__ float sM[NKV][32], sL[NKV][32];
 
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // grid (heads x batch, query blocks): every (sequence, head) of the
+  // longest query block is dispatched before any shorter one
+  const int qb = gridDim.y - 1 - blockIdx.y;
+  const int h = blockIdx.x % a.nh, b = blockIdx.x / a.nh;
   const int g = h / (a.nh / a.nkv);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 5, col = lane & 31;
@@ -114,36 +178,10 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hb][ks], qf[ks], sc[hb], 0, 0, 0);
     }
-    // score register v of half hb holds key key0 + 32 hb + 16 (v / 8) + 8 grp + v % 8
-    const bool diag = key0 + KB - 1 > q0;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + 32 * hb + 16 * (v >> 3) + 8 * grp + (v & 7);
-        float t = sc[hb][v] * a.scale_log2;
-        t = (diag && (key > qi || key >= S)) ? -__builtin_inff() : t;
-        sc[hb][v] = t;
-        mx = fmaxf(mx, t);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: key0 <= q0 <= qi is never masked
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = exp2f(sc[hb][v] - m_new);
-        sc[hb][v] = e;
-        psum += e;
-      }
-    m_run = m_new;
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    // keys past min(qi, S - 1) are masked, in blocks that reach the diagonal
+    softmax_block<HB, DB>(sc, o, m_run, l_run, a.scale_log2, key0 + KB - 1 > q0, min(qi, S - 1) - key0 - 8 * grp);
     if (key0 + KB > S) {  // value columns >= S are padding: zero them
+      const int vlim = S - key0 - 8 * grp;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -152,7 +190,7 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
           for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (key0 + 32 * hb + 16 * hv + 8 * grp + e >= S) vf[hb][db][hv][e] = (f16)0.f;
+              vf[hb][db][hv][e] = 32 * hb + 16 * hv + e < vlim ? vf[hb][db][hv][e] : (f16)0.f;
     }
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -206,6 +244,179 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
       r[4 + e] = (f16)(n1[e] * inv);
     }
     *reinterpret_cast<f16x8*>(out + ((size_t)b * S + q0 + qq) * ld + h * D + c * 8) = r;
+  }
+}
+
+// binary16 path for long sequences (shared key blocks): a workgroup owns 128
+// queries of one (sequence, head), 32 per wave, and walks the 64-key blocks
+// up to its last query once.  Each block's keys [64][D] and V^T columns
+// [D][64] go global -> LDS by DMA into a ring of 3 stages (2 at head_dim
+// 128, where 3 would leave one workgroup per CU), the others ahead of the one
+// being read, and all four waves read them from LDS (one global read
+// per block per workgroup instead of one per wave).  Each wave keeps its own
+// online softmax over every block up to its diagonal, so no merge is needed.
+// LDS rows: a key row is D / 8 + 1 16-byte slots (the extra slot is padding
+// that makes the 32 rows of a fragment read conflict free); a V^T row is 8
+// slots with chunk' = chunk ^ ((d >> 1) & 7).  The MFMA formulation and the
+// key-row permutation are those of the split-key kernel.
+template <int D>
+__global__ __launch_bounds__(256, 2) void phi_attn_prefill_lds_kernel(AttnArgs a) {
+  static_assert(D == 64 || D == 96 || D == 128, "head_dim");
+  constexpr int KB = 64, KS = D / 16, DB = D / 32;
+  constexpr int NSTG = D == 128 ? 2 : 3;                 // stages (2 workgroups per CU in LDS)
+  constexpr int PD = NSTG - 1;                           // blocks in flight ahead of the one read
+  constexpr int KSLOT = D / 8 + 1;                       // 16-byte slots per LDS key row
+  constexpr int NK = KB * KSLOT / 64, NV = D * 8 / 64;   // 1 KB DMA instructions per block
+  constexpr int NI = NK + NV, LPW = ((NK > NV ? NK : NV) + 1) / 2;  // loads per wave and block
+  constexpr int STG = NI * 1024;                          // bytes per stage
+  constexpr int OLD = D + 8;                              // output staging row (f16)
+  static_assert(NK * 64 == KB * KSLOT, "key slots fill whole instructions");
+  static_assert(4 * 32 * OLD * 2 <= NSTG * STG, "output staging fits");
+  static_assert(2 * NSTG * STG <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) char lds[NSTG * STG];
+
+  const int qb = gridDim.y - 1 - blockIdx.y;   // 128-query block, longest first over the whole grid
+  const int h = blockIdx.x % a.nh, b = blockIdx.x / a.nh;
+  const int g = h / (a.nh / a.nkv);
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 5, col = lane & 31;
+  const int S = a.S;
+  const int q0 = qb * 128 + 32 * w;            // this wave's first query
+  const int qi = q0 + col;
+  const int last_q = min(qb * 128 + 127, S - 1);
+  const int nb = last_q / KB + 1;              // key blocks of the workgroup
+  const int wave_last = q0 < S ? min(q0 + 31, S - 1) : -1;  // -1: the wave has no queries
+
+  const f16* Q = reinterpret_cast<const f16*>(a.q) + ((size_t)(b * a.nh + h) * S) * D;
+  const f16* Kp = reinterpret_cast<const f16*>(a.k) + ((size_t)(b * a.nkv + g) * S) * D;
+  const f16* Vt = reinterpret_cast<const f16*>(a.vt) + ((size_t)(b * a.nkv + g) * D) * a.s_pad;
+
+  // DMA work: waves 0 and 1 copy the key rows (instructions 0 .. NK - 1,
+  // alternating), waves 2 and 3 the V^T rows (NK .. NI - 1); a wave with
+  // fewer instructions than LPW repeats its last one, so every wave has LPW
+  // loads in flight per block and one vmcnt count fits all.
+  const bool kwave = w < 2;
+  const int nown = kwave ? NK : NV, wi = w & 1;
+  int lrow[LPW], loff[LPW], ldst[LPW];
+#pragma unroll
+  for (int t = 0; t < LPW; ++t) {
+    const int jj = min(wi + 2 * t, nown - 1 - ((nown - 1 - wi) & 1));  // index among the wave's kind
+    const int sl = jj * 64 + lane;
+    if (kwave) {
+      const int r = sl / KSLOT, c = min(sl - r * KSLOT, D / 8 - 1);  // the padding slot re-reads the last chunk
+      lrow[t] = r;
+      loff[t] = c * 8;
+      ldst[t] = jj * 1024;
+    } else {
+      const int d = sl >> 3, c = (sl & 7) ^ ((d >> 1) & 7);
+      lrow[t] = 0;
+      loff[t] = d * a.s_pad + c * 8;             // + key0: columns < s_pad, inside the buffer
+      ldst[t] = (NK + jj) * 1024;
+    }
+  }
+  auto issue = [&](int blk, int stage) {
+    const int key0 = blk * KB;
+    char* st = lds + stage * STG;
+    if (kwave) {
+#pragma unroll
+      for (int t = 0; t < LPW; ++t) {
+        // key rows past the sequence re-read the last row (their scores are masked)
+        const f16* gsrc = Kp + (size_t)min(key0 + lrow[t], S - 1) * D + loff[t];
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)gsrc, (lds_ptr_t)(st + ldst[t]), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < LPW; ++t)
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(Vt + loff[t] + key0), (lds_ptr_t)(st + ldst[t]), 16, 0, 0);
+    }
+  };
+
+  const int kr = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);  // bits 2 and 3 swapped
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  issue(0, 0);
+  f16x8 qf[KS];
+  {
+    const f16* qrow = Q + (size_t)min(qi, S - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const f16x8*>(qrow + (ks * 2 + grp) * 8);
+  }
+  if (PD > 1 && nb > 1) issue(1, 1);
+  // Wait for the query fragments here, where only block 1's loads are newer,
+  // so that the compiler does not wait for every load in flight at their
+  // first use inside the loop.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  for (int j = 0; j < nb; ++j) {
+    // block j landed: only the (PD - 1) newer blocks' loads may still be in flight
+    if (PD > 1 && j + 1 < nb) PHI_WAIT_VMCNT((PD - 1) * LPW);
+    else PHI_WAIT_VMCNT(0);
+    attn_lds_barrier();  // every wave's share of block j is in LDS; block j - 1's stage is free
+    if (j + PD < nb) issue(j + PD, (j + PD) % NSTG);
+    const int key0 = j * KB;
+    if (key0 > wave_last) continue;            // above this wave's diagonal (barriers still met)
+    const char* stg = lds + (j % NSTG) * STG;
+    const char* ks_base = stg;
+    const char* vs_base = stg + NK * 1024;
+    f32x16 sc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sc[hb] = f32x16{};
+      const char* krow = ks_base + (32 * hb + kr) * KSLOT * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(krow + (ks * 2 + grp) * 16);
+        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sc[hb], 0, 0, 0);
+      }
+    }
+    // keys past min(qi, S - 1) are masked, in blocks that reach the diagonal
+    softmax_block<2, DB>(sc, o, m_run, l_run, a.scale_log2, key0 + KB - 1 > q0, min(qi, S - 1) - key0 - 8 * grp);
+    const bool tail = key0 + KB > S;  // value columns >= S are padding: zero them
+    const int vlim = S - key0;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        f16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (f16)sc[hb][8 * hv + e];
+        const int chunk = 4 * hb + 2 * hv + grp;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + col;
+          f16x8 vf = *reinterpret_cast<const f16x8*>(vs_base + d * 128 + 16 * (chunk ^ ((d >> 1) & 7)));
+          if (tail) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vf[e] = 8 * chunk + e < vlim ? vf[e] : (f16)0.f;
+          }
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
+        }
+      }
+  }
+
+  // normalise, stage [query][d] through LDS, 16-byte stores
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = wave_last >= q0 ? 1.0f / l_tot : 0.f;
+  __syncthreads();  // every wave is done with the stages
+  f16* so = reinterpret_cast<f16*>(lds) + w * 32 * OLD;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) so[col * OLD + db * 32 + 8 * (v >> 2) + 4 * grp + (v & 3)] = (f16)(o[db][v] * inv);
+  __syncthreads();
+  f16* out = reinterpret_cast<f16*>(a.out);
+  const int ld = a.nh * D;
+  constexpr int CH = D / 8;
+  for (int c = lane; c < 32 * CH; c += 64) {
+    const int r = c / CH, ch = c - r * CH;
+    const int qq = q0 + r;
+    if (qq < S)
+      *reinterpret_cast<f16x8*>(out + ((size_t)b * S + qq) * ld + h * D + ch * 8) =
+          *reinterpret_cast<const f16x8*>(so + r * OLD + ch * 8);
   }
 }
 

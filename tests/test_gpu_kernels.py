@@ -144,6 +144,27 @@ def test_attention_f16_head_dim_128(phi, B, S, nh, nkv):
     assert np.all(np.abs(got - ref) <= 2e-3 + 2e-3 * np.abs(ref)), np.abs(got - ref).max()
 
 
+# Launches of at least 384 workgroups of 128 queries take the shared-key-block
+# kernel: ragged sequences (a last query block with one query, so waves with
+# no queries; a last key block with one key), grouped heads, every head width.
+@pytest.mark.parametrize("B,S,nh,nkv,D", [(3, 1000, 16, 4, 96), (1, 1537, 32, 32, 96), (2, 777, 40, 10, 128),
+                                          (4, 600, 24, 8, 64)])
+def test_attention_f16_shared_key_blocks(phi, B, S, nh, nkv, D):
+    assert B * nh * (-(-S // 128)) >= 384
+    _say(f"attention f16 shared blocks D={D} B={B} S={S} nh={nh} nkv={nkv}")
+    q, k, v = _attn_inputs(B, S, nh, nkv, np.float16, 51 + S, scale=1.5, D=D)
+    got = _attn_gpu(phi, q, k, v)
+    ref = _attn_ref(q, k, v)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 2e-3 + 2e-3 * np.abs(ref)), np.abs(got - ref).max()
+
+
+def test_attention_shared_key_blocks_rows_sum_to_one(phi):
+    q, k, v = _attn_inputs(1, 3001, 16, 2, np.float16, 6, scale=2.0)
+    got = _attn_gpu(phi, q, k, np.ones_like(v))
+    assert np.abs(got - 1).max() <= 2e-3
+
+
 @pytest.mark.parametrize("B,S,nh,nkv", [(1, 16, 4, 4), (2, 70, 4, 2)])
 def test_attention_f32(phi, B, S, nh, nkv):
     _say(f"attention f32 B={B} S={S}")
