@@ -451,15 +451,21 @@ struct DecodePlan {
   size_t off_ml, total;
 };
 
-// Splits of whole 64-token chunks per wave (16 pages per workgroup round):
-// 32 pages per split unless that leaves fewer than ~2 workgroups per CU.
+// Pages per split: the largest of 64, 32, 16 that still gives at least 320
+// workgroups (more than one per CU); 16 below that.  Long splits amortise
+// each workgroup's start-up (table and query loads, the first page's
+// latency) and the merge; one split per sequence skips the merge launch.
 DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
   DecodePlan p;
   const int np = (max_ctx + 15) / 16;
   const long units = (long)batch * n_kv_heads;
-  int pps = 32;
-  if (units * ((np + pps - 1) / pps) < 512) pps = 16;
-  if (pps > (np + 15) / 16 * 16) pps = (np + 15) / 16 * 16;
+  int pps = 16;
+  for (int cand : {64, 32}) {
+    if (units * ((np + cand - 1) / cand) >= 320) {
+      pps = cand;
+      break;
+    }
+  }
   p.pages_per_split = pps;
   p.n_split = (np + pps - 1) / pps;
   const size_t parts = (size_t)batch * n_q_heads * p.n_split;
@@ -494,13 +500,13 @@ phi_status decode_attention(const void* q, const void* k_pool, const void* v_poo
   a.scale_log2 = sm_scale * kLog2e;
   const dim3 grid(p.n_split, n_kv_heads, batch);
   switch (n_q_heads / n_kv_heads) {
-    case 1: hipLaunchKernelGGL(phi_decode_split_kernel<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(phi_decode_split_kernel<2>, grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(phi_decode_split_kernel<4>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(phi_decode_split_kernel<8>, grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((phi_decode_stream_kernel<1, 2>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((phi_decode_stream_kernel<2, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((phi_decode_stream_kernel<4, 2>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((phi_decode_stream_kernel<8, 2>), grid, dim3(256), 0, st, a); break;
   }
   if (hipGetLastError() != hipSuccess) return PHI_E_HIP;
-  hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
+  if (p.n_split > 1) hipLaunchKernelGGL(phi_decode_merge_kernel, dim3(batch * n_q_heads), dim3(128), 0, st, a);
   return launched();
 }
 

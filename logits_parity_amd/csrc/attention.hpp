@@ -46,15 +46,6 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(D)
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
-#ifndef PHI_WAIT_VMCNT
-// s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
-#define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
-#endif
-// Workgroup barrier that waits for this wave's LDS operations only.
-__device__ __forceinline__ void attn_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Buffer resource over [base, base + bytes): loads outside read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
@@ -355,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void phi_attn_prefill_lds_kernel(AttnArgs a
     // block j landed: only the (PD - 1) newer blocks' loads may still be in flight
     if (PD > 1 && j + 1 < nb) PHI_WAIT_VMCNT((PD - 1) * LPW);
     else PHI_WAIT_VMCNT(0);
-    attn_lds_barrier();  // every wave's share of block j is in LDS; block j - 1's stage is free
+    lds_barrier();  // every wave's share of block j is in LDS; block j - 1's stage is free
     if (j + PD < nb) issue(j + PD, (j + PD) % NSTG);
     const int key0 = j * KB;
     if (key0 > wave_last) continue;            // above this wave's diagonal (barriers still met)

@@ -14,6 +14,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Address spaces of the direct global -> LDS loads (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the wave-uniform LDS address + 16 * lane).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+// s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
+#define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only.  __syncthreads() would also wait for every outstanding global load,
+// draining DMA stages that are meant to stay in flight; a stage about to be
+// read is waited for explicitly (vmcnt) before this barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float wave_sum(float v) {

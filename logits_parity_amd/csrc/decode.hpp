@@ -3,20 +3,23 @@
 //
 // Split kernel: a workgroup owns one (sequence, KV head, context split) and
 // serves all G query heads of the GQA group from one read of each K/V page.
-// Its 4 waves take chunks of 4 pages (64 tokens) round-robin.  Per chunk a wave
+// Wave w takes pages w, w + 4, ... of the split and streams them through its
+// own LDS ring by direct global -> LDS loads (no VGPR staging), so page
+// reads stay in flight while it computes.  Per page a wave
 //  1. forms the scores S^T[token][head] = K Q^T with v_mfma_f32_16x16x32_f16:
-//     one page is 16 tokens x 128 dims, so 4 MFMAs per page; lane l supplies
-//     key row l % 16 and dims 8 (l / 16) + 32 k straight from the page, and
-//     the query of head l % 16 (zero for l % 16 >= G) as the other operand;
-//  2. updates one running max per head for the whole wave (so the output is
-//     rescaled once per chunk) and the probabilities p = 2^(s - max);
+//     16 tokens x 128 dims, 4 MFMAs; lane l supplies key row l % 16 and dims
+//     8 (l / 16) + 32 k from LDS, and the query of head l % 16 (zero for
+//     l % 16 >= G) as the other operand;
+//  2. updates one running max per head (log2 units) and the probabilities
+//     p = 2^(c s - max), rescaling the output only when a max grew;
 //  3. passes p through a per-wave LDS slot into the layout of the value pass;
 //  4. accumulates o[h][d] += p[h][t] v[t][d] on the VALU: lane l owns dims
-//     16 (l % 8) .. +15 and tokens l / 8 + 8 j of the chunk, reading 16 bytes
-//     of E4M3 per token and decoding them with v_cvt_pk_f32_fp8.
+//     16 (l % 8) .. +15 and tokens l / 8 and l / 8 + 8 of the page, reading 16
+//     bytes of E4M3 per token and decoding them with v_cvt_pk_f32_fp8.
 // At the end the lanes' partial outputs are summed (they share the running
 // max), the 4 waves are merged by log-sum-exp through LDS, and the split's
-// (o unnormalised, max, sum) go to the workspace.  The per-head value scale
+// (o unnormalised, max, sum) go to the workspace; with a single split the
+// kernel normalises and writes the output itself.  The per-head value scale
 // multiplies the final output once.
 //
 // Merge kernel: o = sum_s o_s e^(m_s - m) / sum_s l_s e^(m_s - m) * scale.
@@ -41,130 +44,151 @@ struct DecodeArgs {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int G>
-__global__ __launch_bounds__(256) void phi_decode_split_kernel(DecodeArgs a) {
-  constexpr int D = 128, PG = 16, CH = 4;  // pages per chunk
+// Each wave's ring has NST one-page stages, filled NST - 1 pages ahead of
+// the page it computes; the four rings are independent (no barrier until the
+// final merge).  Stage layout: keys [16 tokens][128 dims] binary16 with the
+// 16-byte chunk c of token row r stored at slot c ^ r (conflict-free
+// fragment reads), then the value codes [16][128] as in the page.
+template <int G, int NST>
+__global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a) {
+  constexpr int D = 128, PG = 16;
+  constexpr int KBY = PG * D * 2, VBY = PG * D, SB = KBY + VBY, WB = NST * SB;
+  constexpr int LPP = KBY / 1024 + VBY / 1024;  // loads per page and wave
   static_assert(G >= 1 && G <= 8, "GQA group");
-  __shared__ float sP[4][CH * PG][G];      // per wave: probabilities of the chunk
-  __shared__ float s_o[4][G][D];
-  __shared__ float s_ml[4][G][2];
+  static_assert(NST >= 2 && (NST - 2) * LPP <= 63, "ring depth");
+  static_assert(4 * G * D * 4 + 4 * G * 2 * 4 <= 4 * WB, "merge staging fits in the rings");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * WB];
+  __shared__ float sP[4][PG][G];
   __shared__ int s_err[4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int hl = lane & 15, kq = lane >> 4;      // score layout: head column, token quad
-  const int dq = lane & 7, t8 = lane >> 3;       // value layout: dims 16 dq.., tokens t8 + 8 j
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane & 15, kq = lane >> 4;  // score layout: head column, token quad
+  const int dq = lane & 7, t8 = lane >> 3;   // value layout: dims 16 dq .., tokens t8 and t8 + 8
   const int L = a.ctx_lens[b];
   bool err = L < 1 || L > a.max_pages * PG;
   const int np = err ? 0 : (L + PG - 1) / PG;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(np, p_begin + a.pages_per_split);
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  int nw = p_end - p_begin - w > 0 ? (p_end - p_begin - w + 3) / 4 : 0;  // <= 64 (host: pages_per_split <= 256)
 
-  // query operand: head hl (zero beyond the group), dims 32 k + 8 kq .. +7
+  // query operand: head hl (zero beyond the group), dims 32 k + 8 kq .. +7;
+  // loaded together with the block-table entries, so both cost one latency
   f16x8 qf[4];
+  {
+    const f16* qrow = a.q + ((size_t)b * a.Hq + g * G + min(hl, G - 1)) * D + 8 * kq;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (hl < G) qf[k] = *reinterpret_cast<const f16x8*>(a.q + ((size_t)b * a.Hq + g * G + hl) * D + 32 * k + 8 * kq);
-    else qf[k] = f16x8{};
+    for (int k = 0; k < 4; ++k) qf[k] = *reinterpret_cast<const f16x8*>(qrow + 32 * k);
   }
+  // physical page of the wave's page i in lane i (lanes past nw re-read an entry in the row)
+  const int ti = min(p_begin + w + 4 * min(lane, max(nw - 1, 0)), a.max_pages - 1);
+  int my_phys = a.block_table[(size_t)b * a.max_pages + ti];
+  if (lane < nw && (my_phys < 0 || my_phys >= a.n_pages)) err = true;
+  if (__any(err)) {  // the split's result becomes NaN; read nothing
+    err = true;
+    nw = 0;
+  }
+  if (hl >= G) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qf[k] = f16x8{};
+  }
+
+  char* ring = lds + w * WB;
+  auto issue = [&](int i) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, i);
+    char* st = ring + (i % NST) * SB;
+    const char* kp = reinterpret_cast<const char*>(a.k_pool + ((size_t)phys * a.Hkv + g) * PG * D);
+    const char* vp = reinterpret_cast<const char*>(a.v_pool + ((size_t)phys * a.Hkv + g) * PG * D);
+    const int r0 = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int j = 0; j < KBY / 1024; ++j) {  // token rows 4 j .. 4 j + 3; LDS slot c of row r takes chunk c ^ r
+      const int r = 4 * j + r0;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(kp + r * 256 + ((c ^ r) << 4)), (lds_ptr_t)(st + j * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VBY / 1024; ++j)
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vp + j * 1024 + lane * 16), (lds_ptr_t)(st + KBY + j * 1024), 16, 0, 0);
+  };
+
+  for (int i = 0; i < NST - 1 && i < nw; ++i) issue(i);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(qf[k]));  // the query lands before the loop
 
   float o[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int d = 0; d < 16; ++d) o[h][d] = 0.f;
-  float m_run = -__builtin_inff();  // lanes hl < G: running max of head hl
+  float m_run = -__builtin_inff();  // lanes hl < G: running max of head hl (log2 units)
   float l_run = 0.f;                // lanes hl < G: partial sum over this lane's tokens
+  const float c2 = a.scale_log2;
 
-  for (int c0 = p_begin + CH * w; c0 < p_end; c0 += CH * 4) {
-    // physical pages of the chunk; pages past the split reuse the first one (masked)
-    int phys[CH];
-    bool bad = false;
-#pragma unroll
-    for (int pi = 0; pi < CH; ++pi) {
-      const int p = c0 + pi < p_end ? c0 + pi : c0;
-      phys[pi] = bt[p];
-      bad |= phys[pi] < 0 || phys[pi] >= a.n_pages;
-    }
-    if (bad) { err = true; break; }
+  for (int i = 0; i < nw; ++i) {
+    // page i landed; only the newer pages' loads (NST - 2 of them at most) may be in flight
+    if (NST > 2 && i + 1 < nw) PHI_WAIT_VMCNT((NST - 2) * LPP);
+    else PHI_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");  // the page's LDS reads stay after the wait
+    if (i + NST - 1 < nw) issue(i + NST - 1);  // into the stage of page i - 1, whose reads are done
+    const char* st = ring + (i % NST) * SB;
+    const int pg = p_begin + w + 4 * i;
 
-    // 1. scores: per page, 16 tokens x 16 heads
-    f32x4 sc[CH];
+    // 1. scores of the page's 16 tokens for heads hl
+    f32x4 sc = f32x4{};
 #pragma unroll
-    for (int pi = 0; pi < CH; ++pi) {
-      const f16* kp = a.k_pool + (((size_t)phys[pi] * a.Hkv + g) * PG + hl) * D + 8 * kq;
-      f16x8 kf[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) kf[k] = *reinterpret_cast<const f16x8*>(kp + 32 * k);
-      sc[pi] = f32x4{};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sc[pi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[k], qf[k], sc[pi], 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      const f16x8 kf = *reinterpret_cast<const f16x8*>(st + hl * 256 + (((kq + 4 * k) ^ hl) << 4));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[k], sc, 0, 0, 0);
     }
-    // value bytes of this lane's 8 tokens (issued early, used after the softmax)
-    i32x4 vb[8];
+    const bool tail = (pg + 1) * PG > L;
+    if (tail) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = t8 + 8 * j;  // token within the chunk: page j / 2, slot t % 16
-      vb[j] = *reinterpret_cast<const i32x4*>(a.v_pool + (((size_t)phys[j >> 1] * a.Hkv + g) * PG + (t & 15)) * D + 16 * dq);
+      for (int j = 0; j < 4; ++j) sc[j] = pg * PG + 4 * kq + j < L ? sc[j] : -__builtin_inff();
     }
-
-    // 2. running max per head over the chunk; lanes hl, hl+16, hl+32, hl+48 share a head
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int pi = 0; pi < CH; ++pi)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = (c0 + pi) * PG + 4 * kq + j;
-        float s = sc[pi][j] * a.scale_log2;
-        if (c0 + pi >= p_end || tok >= L) s = -__builtin_inff();
-        sc[pi][j] = s;
-        mx = fmaxf(mx, s);
-      }
+    // 2. running max per head (lanes hl, hl + 16, hl + 32, hl + 48 share a head)
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: the chunk's first token is valid
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    const float m_new = fmaxf(m_run, mx * c2);  // finite: the page's first token is valid
     float ps = 0.f;
 #pragma unroll
-    for (int pi = 0; pi < CH; ++pi)
+    for (int j = 0; j < 4; ++j) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[j], c2, -m_new));
+      ps += p;
+      if (hl < G) sP[w][4 * kq + j][hl] = p;
+    }
+    if (__ballot(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first page
+      l_run *= alpha;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = exp2f(sc[pi][j] - m_new);
-        ps += p;
-        if (hl < G) sP[w][pi * PG + 4 * kq + j][hl] = p;
+      for (int h = 0; h < G; ++h) {
+        const float al = __shfl(alpha, h);
+#pragma unroll
+        for (int d = 0; d < 16; ++d) o[h][d] *= al;
       }
-    l_run = l_run * alpha + ps;
-    __builtin_amdgcn_wave_barrier();  // LDS writes above stay before the reads below (in-order per wave)
+    }
+    m_run = m_new;
+    l_run += ps;
+    __builtin_amdgcn_wave_barrier();  // the LDS writes above stay before the reads below (in order per wave)
 
-    // 3. per-head rescale factors to every lane; probabilities of this lane's tokens
-    float al[G];
+    // 3. o += p v over this lane's two tokens
 #pragma unroll
-    for (int h = 0; h < G; ++h) al[h] = __shfl(alpha, h);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 16; ++d) o[h][d] *= al[h];
-
-    // 4. o += p v
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = t8 + 8 * j;
-      // slots past the context may hold any bytes (even NaN codes): skip them
-      if (c0 + (j >> 1) >= p_end || c0 * PG + t >= L) continue;
+    for (int jj = 0; jj < 2; ++jj) {
+      const int t = t8 + 8 * jj;
+      const i32x4 vb = *reinterpret_cast<const i32x4*>(st + KBY + t * D + 16 * dq);
       float pv[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) pv[h] = sP[w][t][h];
+      // slots past the context may hold any bytes (even NaN codes): weight 0 and value 0
+      const bool live = !tail || pg * PG + t < L;
       float vf[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vb[j][i], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vb[j][i], true);
-        vf[4 * i + 0] = lo[0];
-        vf[4 * i + 1] = lo[1];
-        vf[4 * i + 2] = hi[0];
-        vf[4 * i + 3] = hi[1];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vb[q4], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vb[q4], true);
+        vf[4 * q4 + 0] = live ? lo[0] : 0.f;
+        vf[4 * q4 + 1] = live ? lo[1] : 0.f;
+        vf[4 * q4 + 2] = live ? hi[0] : 0.f;
+        vf[4 * q4 + 3] = live ? hi[1] : 0.f;
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -182,32 +206,39 @@ __global__ __launch_bounds__(256) void phi_decode_split_kernel(DecodeArgs a) {
       for (int d = 0; d < 16; ++d) o[h][d] += __shfl_xor(o[h][d], mask);
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const int any_err = __any(err);
+  __syncthreads();  // every wave is done with its ring: reuse it for the merge
+  float* s_o = reinterpret_cast<float*>(lds);            // [4][G][D]
+  float* s_ml = s_o + 4 * G * D;                           // [4][G][2]
   if (lane < 8) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 16; ++d) s_o[w][h][16 * dq + d] = o[h][d];
+      for (int d = 0; d < 16; ++d) s_o[(w * G + h) * D + 16 * dq + d] = o[h][d];
   }
   if (lane < G) {
-    s_ml[w][lane][0] = m_run;
-    s_ml[w][lane][1] = l_tot;
+    s_ml[(w * G + lane) * 2 + 0] = m_run;
+    s_ml[(w * G + lane) * 2 + 1] = l_tot;
   }
-  if (lane == 0) s_err[w] = any_err;
+  if (lane == 0) s_err[w] = err;
   __syncthreads();
   const bool bad = s_err[0] | s_err[1] | s_err[2] | s_err[3];
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx - h * D;
     float mn = -__builtin_inff();
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mn = fmaxf(mn, s_ml[ww][h][0]);
+    for (int ww = 0; ww < 4; ++ww) mn = fmaxf(mn, s_ml[(ww * G + h) * 2]);
     float ls = 0.f, os = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float mw = s_ml[ww][h][0];
-      const float f = mw == -__builtin_inff() ? 0.f : exp2f(mw - mn);
-      ls += s_ml[ww][h][1] * f;
-      os += s_o[ww][h][d] * f;
+      const float mw = s_ml[(ww * G + h) * 2];
+      const float f = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - mn);
+      ls += s_ml[(ww * G + h) * 2 + 1] * f;
+      os += s_o[(ww * G + h) * D + d] * f;
+    }
+    if (a.n_split == 1) {  // the whole context in one split: normalise here, no merge launch
+      const float r = (!bad && ls > 0.f) ? os / ls * a.v_scale[g] : __builtin_nanf("");
+      a.out[(size_t)(b * a.Hq + g * G + h) * D + d] = (f16)r;
+      continue;
     }
     const size_t pi = ((size_t)(b * a.Hq + g * G + h) * a.n_split + split);
     a.part_o[pi * D + d] = os;

@@ -107,18 +107,6 @@ __device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
 }
 
 // ---------------------------------------------------------------- MFMA core
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
-
-// s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
-#define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
-
-// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
-// only.  __syncthreads() would also wait for every outstanding global load,
-// draining the DMA stages that are meant to stay in flight; the DMA stage a
-// k-step reads is waited for explicitly (vmcnt) before this barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
 // Eight int8 codes (two dwords) -> binary16, exactly: with the sign bit

@@ -60,6 +60,22 @@ def test_decode_ragged_contexts(phi, G):
     assert rel.max() <= 2e-3, rel.max()
 
 
+# Launches with at least 320 (sequence, KV head, split) workgroups use
+# 64-page splits: one split per sequence (normalised in the split kernel, no
+# merge) at max_ctx <= 1024, two splits (merged, the second empty for the
+# shorter sequences) above.
+@pytest.mark.parametrize("max_ctx", [1000, 1500])
+def test_decode_long_splits_ragged(phi, max_ctx):
+    wl = synth.DecodeWorkload("t", batch=40, ctx=max_ctx, n_q_heads=16, n_kv_heads=8)
+    lens = [max_ctx - 37 * i for i in range(40)]
+    lens = [max(1, x) for x in lens]
+    _say(f"decode long splits max_ctx={max_ctx}")
+    d = synth.decode_inputs(wl, ctx_lens=lens)
+    got = _gpu(phi, d, max_ctx=max_ctx)
+    rel = _rel(got, _ref(d))
+    assert rel.max() <= 2e-3, rel.max()
+
+
 def test_decode_page_permutation_is_invisible(phi):
     wl = synth.DecodeWorkload("t", batch=4, ctx=500, n_q_heads=8, n_kv_heads=2)
     d = synth.decode_inputs(wl)
