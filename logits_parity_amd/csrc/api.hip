@@ -77,7 +77,8 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 
 // Tile shape per GEMM role and token count: large wave tiles keep LDS traffic
 // per MFMA low; at small M the residual GEMMs (N = hidden) have too few tiles
-// for 256 CUs, so K is split until every CU has work.  int8 and binary16
+// for 256 CUs, so K is split into as many ranges as give one even round of
+// workgroups (any count: 5 at 512 tokens, 240 workgroups of 256 x 128).  int8 and binary16
 // weights share the plans (both go global -> LDS by DMA).
 GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   GemmPlan p{};
@@ -85,15 +86,16 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
   else if (epi == EPI_SILU) p.cfg = M >= 1024 ? C_L : C_M;
   else if (epi == EPI_F32) p.cfg = C_L;
-  else p.cfg = M >= 2048 ? C_M : C_S;
+  else p.cfg = C_M;
   int bm, bn;
   cfg_dims(p.cfg, bm, bn);
   p.tiles_m = (M + bm - 1) / bm;
   p.tiles_n = epi == EPI_SILU ? (N / 2) / (bn / 2) : (N + bn - 1) / bn;
   const int nk = K / 64;
   int s = 1;
-  if (epi == EPI_RESID)
-    while (p.tiles_m * p.tiles_n * s < kCUs && nk / (2 * s) >= 4) s *= 2;
+  // residual GEMMs: as many K splits as keep one round of at most 256
+  // workgroups (one per CU) and at least 4 k-steps per split
+  if (epi == EPI_RESID) s = std::max(1, std::min(kCUs / (p.tiles_m * p.tiles_n), nk / 4));
   p.kpt = (nk + s - 1) / s;
   p.splits = (nk + p.kpt - 1) / p.kpt;
   return p;
