@@ -453,16 +453,17 @@ struct DecodePlan {
   size_t off_ml, total;
 };
 
-// Pages per split: the largest of 64, 32, 16 that still gives at least 320
-// workgroups (more than one per CU); 16 below that.  Long splits amortise
-// each workgroup's start-up (table and query loads, the first page's
-// latency) and the merge; one split per sequence skips the merge launch.
+// Pages per split: the largest of 256, 128, 64, 32, 16 that still gives at
+// least 320 workgroups (more than one per CU); 16 below that.  Long splits
+// amortise each workgroup's start-up (table and query loads, the first
+// page's latency) and the merge; one split per sequence skips the merge
+// launch.  (At most 256 pages per split: 64 per wave, one table entry per lane.)
 DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
   DecodePlan p;
   const int np = (max_ctx + 15) / 16;
   const long units = (long)batch * n_kv_heads;
   int pps = 16;
-  for (int cand : {64, 32}) {
+  for (int cand : {256, 128, 64, 32}) {
     if (units * ((np + cand - 1) / cand) >= 320) {
       pps = cand;
       break;

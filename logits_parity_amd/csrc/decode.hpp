@@ -12,12 +12,12 @@
 //     l % 16 >= G) as the other operand;
 //  2. updates one running max per head (log2 units) and the probabilities
 //     p = 2^(c s - max), rescaling the output only when a max grew;
-//  3. passes p through a per-wave LDS slot into the layout of the value pass;
-//  4. accumulates o[h][d] += p[h][t] v[t][d] on the VALU: lane l owns dims
-//     16 (l % 8) .. +15 and tokens l / 8 and l / 8 + 8 of the page, reading 16
-//     bytes of E4M3 per token and decoding them with v_cvt_pk_f32_fp8.
-// At the end the lanes' partial outputs are summed (they share the running
-// max), the 4 waves are merged by log-sum-exp through LDS, and the split's
+//  3. accumulates O^T += V^T P^T with v_mfma_f32_16x16x16_f16: the score
+//     registers already are the P^T operand (tokens 4 (l / 16) + j of head
+//     l % 16), rounded to binary16; the V^T operand is built from 8 bytes of
+//     E4M3 per token (dims 8 (l % 16) .. +7 of the lane's 4 tokens), transposed
+//     bytewise by v_perm_b32 and widened exactly to binary16.
+// At the end the 4 waves are merged by log-sum-exp through LDS, and the split's
 // (o unnormalised, max, sum) go to the workspace; with a single split the
 // kernel normalises and writes the output itself.  The per-head value scale
 // multiplies the final output once.
@@ -58,13 +58,11 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
   static_assert(NST >= 2 && (NST - 2) * LPP <= 63, "ring depth");
   static_assert(4 * G * D * 4 + 4 * G * 2 * 4 <= 4 * WB, "merge staging fits in the rings");
   __shared__ __attribute__((aligned(1024))) char lds[4 * WB];
-  __shared__ float sP[4][PG][G];
   __shared__ int s_err[4];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane & 15, kq = lane >> 4;  // score layout: head column, token quad
-  const int dq = lane & 7, t8 = lane >> 3;   // value layout: dims 16 dq .., tokens t8 and t8 + 8
   const int L = a.ctx_lens[b];
   bool err = L < 1 || L > a.max_pages * PG;
   const int np = err ? 0 : (L + PG - 1) / PG;
@@ -114,13 +112,15 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
 #pragma unroll
   for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(qf[k]));  // the query lands before the loop
 
-  float o[G][16];
+  // O^T += V^T P^T by v_mfma_f32_16x16x16_f16, one MFMA per 8 dims of the
+  // head: block db holds dims 8 r + db at MFMA row r, column = head, so lane l
+  // accumulates head hl at dims 8 (4 kq + j) + db, j = 0..3 (its own head's
+  // rows: the rescale needs no exchange)
+  f32x4 acc[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int d = 0; d < 16; ++d) o[h][d] = 0.f;
-  float m_run = -__builtin_inff();  // lanes hl < G: running max of head hl (log2 units)
-  float l_run = 0.f;                // lanes hl < G: partial sum over this lane's tokens
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4{};
+  float m_run = -__builtin_inff();  // running max of head hl (log2 units)
+  float l_run = 0.f;                // partial sum over this lane's tokens
   const float c2 = a.scale_log2;
 
   for (int i = 0; i < nw; ++i) {
@@ -132,17 +132,27 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
     const char* st = ring + (i % NST) * SB;
     const int pg = p_begin + w + 4 * i;
 
-    // 1. scores of the page's 16 tokens for heads hl
+    // 1. scores of the page's 16 tokens for heads hl: lane l holds tokens 4 kq + j
     f32x4 sc = f32x4{};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const f16x8 kf = *reinterpret_cast<const f16x8*>(st + hl * 256 + (((kq + 4 * k) ^ hl) << 4));
       sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[k], sc, 0, 0, 0);
     }
+    // value codes of the lane's 4 tokens, dims 8 hl .. 8 hl + 7 (issued early)
+    uint2 vw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vw[j] = *reinterpret_cast<const uint2*>(st + KBY + (4 * kq + j) * D + 8 * hl);
     const bool tail = (pg + 1) * PG > L;
     if (tail) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sc[j] = pg * PG + 4 * kq + j < L ? sc[j] : -__builtin_inff();
+      for (int j = 0; j < 4; ++j) {
+        const bool live = pg * PG + 4 * kq + j < L;
+        sc[j] = live ? sc[j] : -__builtin_inff();
+        // slots past the context may hold any bytes (even NaN codes): code 0 there
+        vw[j].x = live ? vw[j].x : 0u;
+        vw[j].y = live ? vw[j].y : 0u;
+      }
     }
     // 2. running max per head (lanes hl, hl + 16, hl + 32, hl + 48 share a head)
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -152,68 +162,56 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sc[j], c2, -m_new));
-      ps += p;
-      if (hl < G) sP[w][4 * kq + j][hl] = p;
+      sc[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], c2, -m_new));
+      ps += sc[j];
     }
     if (__ballot(m_new > m_run)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first page
       l_run *= alpha;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = __shfl(alpha, h);
-#pragma unroll
-        for (int d = 0; d < 16; ++d) o[h][d] *= al;
-      }
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
     }
     m_run = m_new;
     l_run += ps;
-    __builtin_amdgcn_wave_barrier();  // the LDS writes above stay before the reads below (in order per wave)
 
-    // 3. o += p v over this lane's two tokens
+    // 3. P^T operand (binary16, nearest) and the V^T operands: the 4 tokens'
+    // words are transposed bytewise so that word db holds dim 8 hl + db of
+    // the 4 tokens; E4M3 widens exactly to binary16
+    const f16x4 pf = {(f16)sc[0], (f16)sc[1], (f16)sc[2], (f16)sc[3]};
+    uint32_t cw[8];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int t = t8 + 8 * jj;
-      const i32x4 vb = *reinterpret_cast<const i32x4*>(st + KBY + t * D + 16 * dq);
-      float pv[G];
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t a0 = hh ? vw[0].y : vw[0].x, a1 = hh ? vw[1].y : vw[1].x;
+      const uint32_t a2 = hh ? vw[2].y : vw[2].x, a3 = hh ? vw[3].y : vw[3].x;
+      const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u), t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+      const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u), t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+      cw[4 * hh + 0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+      cw[4 * hh + 1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+      cw[4 * hh + 2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+      cw[4 * hh + 3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+    }
 #pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = sP[w][t][h];
-      // slots past the context may hold any bytes (even NaN codes): weight 0 and value 0
-      const bool live = !tail || pg * PG + t < L;
-      float vf[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vb[q4], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vb[q4], true);
-        vf[4 * q4 + 0] = live ? lo[0] : 0.f;
-        vf[4 * q4 + 1] = live ? lo[1] : 0.f;
-        vf[4 * q4 + 2] = live ? hi[0] : 0.f;
-        vf[4 * q4 + 3] = live ? hi[1] : 0.f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int d = 0; d < 16; ++d) o[h][d] = fmaf(pv[h], vf[d], o[h][d]);
+    for (int db = 0; db < 8; ++db) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[db], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[db], true);
+      // exact: every E4M3 value is a binary16 value, so round-toward-zero packing loses nothing
+      const f16x2 l2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
+      const f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1]));
+      const f16x4 vf = {l2[0], l2[1], h2[0], h2[1]};
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf, acc[db], 0, 0, 0);
     }
   }
 
-  // lanes of one dim group share the running max: plain sums over t8
-#pragma unroll
-  for (int mask = 8; mask < 64; mask <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 16; ++d) o[h][d] += __shfl_xor(o[h][d], mask);
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   __syncthreads();  // every wave is done with its ring: reuse it for the merge
   float* s_o = reinterpret_cast<float*>(lds);            // [4][G][D]
   float* s_ml = s_o + 4 * G * D;                           // [4][G][2]
-  if (lane < 8) {
+  if (hl < G) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int d = 0; d < 16; ++d) s_o[(w * G + h) * D + 16 * dq + d] = o[h][d];
+      for (int j = 0; j < 4; ++j) s_o[(w * G + hl) * D + 8 * (4 * kq + j) + db] = acc[db][j];
   }
   if (lane < G) {
     s_ml[(w * G + lane) * 2 + 0] = m_run;
