@@ -86,7 +86,14 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
   else if (epi == EPI_SILU) p.cfg = M >= 1024 ? C_L : C_M;
   else if (epi == EPI_F32) p.cfg = C_L;
-  else p.cfg = C_M;
+  else {
+    // 256 x 192 when the output width divides and it gives whole rounds of
+    // 256 workgroups without splitting K (384 tiles of 256 x 128 would leave
+    // the second round half empty); 256 x 128 otherwise
+    p.cfg = C_M;
+    const long t192 = (long)((M + 255) / 256) * (N / 192);
+    if (N % 192 == 0 && t192 >= kCUs && t192 % kCUs == 0) p.cfg = C_QL;
+  }
   int bm, bn;
   cfg_dims(p.cfg, bm, bn);
   p.tiles_m = (M + bm - 1) / bm;
@@ -133,6 +140,7 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
     launch_mfma<CfgL, W8, EPI>(a, st);
   } else {
     if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st);
+    else if (cfg == C_QL) launch_mfma<CfgQL, W8, EPI>(a, st);
     else launch_mfma<CfgS, W8, EPI>(a, st);
   }
 }
