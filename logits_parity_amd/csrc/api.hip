@@ -58,8 +58,16 @@ using CfgQ64 = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64 (one 64-wide head
 enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64 };
 
 struct GemmPlan {
-  int cfg, tiles_m, tiles_n, splits, kpt;
+  int cfg, tiles_m, tiles_n, splits, kpt, group_m;
 };
+
+#ifndef PHI_GEMM_GROUP_M
+#define PHI_GEMM_GROUP_M 8
+#endif
+// M-tiles per tile group when there are more M-tiles than that: the 32
+// workgroups that run together on an XCD then cover a block of 8 x 4 tiles
+// (12 distinct A and W tiles in its L2) instead of a column of all M-tiles.
+constexpr int kGemmGroupM = PHI_GEMM_GROUP_M;
 
 constexpr int kCUs = 256;
 
@@ -105,6 +113,7 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   if (epi == EPI_RESID) s = std::max(1, std::min(kCUs / (p.tiles_m * p.tiles_n), nk / 4));
   p.kpt = (nk + s - 1) / s;
   p.splits = (nk + p.kpt - 1) / p.kpt;
+  p.group_m = std::min(p.tiles_m, kGemmGroupM);
   return p;
 }
 
@@ -222,6 +231,7 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
   a.tiles_n = p.tiles_n;
   a.splits = p.splits;
   a.kt_per_split = p.kpt;
+  a.group_m = p.group_m;
   const bool w8 = wtype == PHI_WT_I8;
   if constexpr (EPI == EPI_RESID) {
     if (p.splits > 1) {

@@ -20,6 +20,9 @@ constexpr int kWave = 64;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
+// Cache-policy operand of global loads: non-temporal (streamed data).
+constexpr int kCacheNT = 2;
+
 // s_waitcnt with only vmcnt constrained (vmcnt bits [3:0] and [15:14]).
 #define PHI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 

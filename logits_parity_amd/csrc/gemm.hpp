@@ -57,6 +57,7 @@ struct GemmArgs {
   const void* scale;  // binary16 [N] (int8 weights)
   int M, N, K;        // N = rows of W (2 I for the fused gate/up)
   int tiles_m, tiles_n, splits, kt_per_split;
+  int group_m;        // M-tiles per tile group (1 <= group_m <= tiles_m)
   float* out;         // EPI_F32: [M][ldo]; EPI_PARTIAL: [splits][M][N]
   int ldo;
   float* x;           // EPI_RESID: [M][ldx]
@@ -164,9 +165,17 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   const int n_units = a.tiles_m * a.tiles_n * a.splits;
   const int unit = xcd_swizzle(blockIdx.x, gridDim.x);
   if (unit >= n_units) return;
-  const int tm = unit % a.tiles_m;
-  const int tn = (unit / a.tiles_m) % a.tiles_n;
-  const int split = unit / (a.tiles_m * a.tiles_n);
+  // units walk group_m M-tiles fastest, then the N-tiles, then the next group
+  // of M-tiles: the workgroups running together on one XCD cover a block of
+  // group_m x (32 / group_m) tiles and share its A and W tiles in L2
+  const int per_split = a.tiles_m * a.tiles_n;
+  const int split = unit / per_split;
+  const int u = unit - split * per_split;
+  const int tgroup = u / (a.group_m * a.tiles_n);
+  const int rem = u - tgroup * a.group_m * a.tiles_n;
+  const int gm = min(a.group_m, a.tiles_m - tgroup * a.group_m);
+  const int tm = tgroup * a.group_m + rem % gm;
+  const int tn = rem / gm;
   const int m0 = tm * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -177,13 +186,16 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   // rows x K within int32): instruction j = wave + NW * t fills LDS bytes
   // [1024 j, 1024 j + 1024) of the stage; the lane's 16-byte slot holds a
   // swizzled chunk of one row
+  // A stage's first INS_A instructions are A rows, the rest W rows; with
+  // INS_A a multiple of NW, instruction t of every wave is of one kind.
+  static_assert(INS_A % NW == 0, "A / W split of the DMA instructions");
+  constexpr int TA_ = INS_A / NW;  // instructions t < TA_ load A
   int src_off[LPW > 0 ? LPW : 1];
-  bool src_is_w[LPW > 0 ? LPW : 1];
 #pragma unroll
   for (int t = 0; t < LPW; ++t) {
     const int j = wave + NW * t;
     const int s = j * 64 + lane;
-    const bool is_w = j >= INS_A;
+    const bool is_w = t >= TA_;
     if (!is_w) {
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
       src_off[t] = (m0 + r < a.M ? m0 + r : a.M - 1) * K + c * 8;
@@ -194,7 +206,6 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
       const int sw = s - INS_A * 64, r = sw >> 3, c = (sw & 7) ^ ((r >> 1) & 7);
       src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 8;
     }
-    src_is_w[t] = is_w;
   }
   const f16* Wf = reinterpret_cast<const f16*>(a.W);
   const int8_t* W8p = reinterpret_cast<const int8_t*>(a.W);
@@ -204,11 +215,12 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
       const int j = wave + NW * t;
-      const void* g;
-      if (!src_is_w[t]) g = A + src_off[t] + k0;
-      else if constexpr (W8) g = W8p + src_off[t] + k0;
-      else g = Wf + src_off[t] + k0;
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024), 16, 0, 0);
+      lds_ptr_t dst = (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024);
+      // weights are streamed once per tile row: non-temporal, so that they do
+      // not push the activation tiles (re-read by every N-tile) out of L2
+      if (t < TA_) __builtin_amdgcn_global_load_lds((glb_ptr_t)(A + src_off[t] + k0), dst, 16, 0, 0);
+      else if constexpr (W8) __builtin_amdgcn_global_load_lds((glb_ptr_t)(W8p + src_off[t] + k0), dst, 16, 0, kCacheNT);
+      else __builtin_amdgcn_global_load_lds((glb_ptr_t)(Wf + src_off[t] + k0), dst, 16, 0, kCacheNT);
     }
   };
 
