@@ -119,10 +119,11 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
 
 // LDS stages of a tile.  Tiles whose two stages leave room for a second
 // workgroup per CU keep 2 (the other workgroup covers the load latency);
-// larger tiles take 3 when they fit in 152 KB.  int8 weights take half the
-// bytes of binary16 ones.
+// larger tiles take 3 when they fit in 152 KB.  int8 weights stage their
+// copies in registers (two register sets over two LDS stages).
 template <class C, bool W8>
 constexpr int gemm_stages() {
+  if (W8) return 2;
   constexpr int stage_bytes = C::BM * 64 * 2 + C::BN * 64 * (W8 ? 1 : 2);
   if (2 * stage_bytes <= 64 * 1024) return 2;
   return 3 * stage_bytes <= 152 * 1024 ? 3 : 2;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
   constexpr int KBY = PG * D * 2, VBY = PG * D, SB = KBY + VBY, WB = NST * SB;
   constexpr int LPP = KBY / 1024 + VBY / 1024;  // loads per page and wave
   static_assert(G >= 1 && G <= 8, "GQA group");
-  static_assert(NST >= 2 && (NST - 2) * LPP <= 63, "ring depth");
+  static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPP <= 63, "ring depth");
   static_assert(4 * G * D * 4 + 4 * G * 2 * 4 <= 4 * WB, "merge staging fits in the rings");
   __shared__ __attribute__((aligned(1024))) char lds[4 * WB];
   __shared__ int s_err[4];
@@ -125,8 +125,10 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
 
   for (int i = 0; i < nw; ++i) {
     // page i landed; only the newer pages' loads (NST - 2 of them at most) may be in flight
-    if (NST > 2 && i + 1 < nw) PHI_WAIT_VMCNT((NST - 2) * LPP);
-    else PHI_WAIT_VMCNT(0);
+    const int newer = min(NST - 2, nw - 1 - i);
+    if (newer <= 0) PHI_WAIT_VMCNT(0);
+    else if (newer == 1) PHI_WAIT_VMCNT(LPP);
+    else PHI_WAIT_VMCNT(2 * LPP);
     asm volatile("" ::: "memory");  // the page's LDS reads stay after the wait
     if (i + NST - 1 < nw) issue(i + NST - 1);  // into the stage of page i - 1, whose reads are done
     const char* st = ring + (i % NST) * SB;

@@ -45,6 +45,8 @@
 //               [B][heads][S][96], V to V^T [B][kv_heads][96][s_pad].
 // fp32 core (float32 model): a SIMT kernel with an LDS-staged epilogue.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace phi {
@@ -139,6 +141,9 @@ struct TileCfg {
 
 template <class C, bool W8, int EPI, int NS>
 __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
+  // int8 weights take the register-staged copy (measured faster for their
+  // 64-byte rows); binary16 operands go global -> LDS by DMA
+  constexpr bool VG = W8;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
   constexpr int NT = C::NT, NW = C::NW, BK = 64;
   static_assert(NS >= 2 && NS <= 4, "stages");
@@ -230,69 +235,124 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  const int kt0 = split * a.kt_per_split;
-  const int kt1 = min(K / BK, kt0 + a.kt_per_split);
-  // stages kt0 .. kt0 + NS - 2 in flight before the first k-step
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
-    if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int rel = kt - kt0;
-    f16* cur = smem + (rel % NS) * STAGE;
-    f16* nxt = smem + ((rel + NS - 1) % NS) * STAGE;  // the stage read in step kt - 1
-    // wait for this wave's DMA of stage kt; the newer stages stay in flight
-    const int newer = min(NS - 2, kt1 - 1 - kt);
-    if (newer <= 0) PHI_WAIT_VMCNT(0);
-    else if (newer == 1) PHI_WAIT_VMCNT(LPW);
-    else PHI_WAIT_VMCNT(2 * LPW);
-    lds_barrier();
-    if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
-    f16x8 af[2][TM], bf[2][TN];
-    const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
-    // B fragments first, then A in MFMA order: the first MFMAs of a step
-    // wait only for the oldest reads, the last reads overlap with them
-    auto ld = [&](int kk, f16x8* fa, f16x8* fb) {
-      const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + (lane & 31);
-        if constexpr (W8) {
-          const uint2 q = *reinterpret_cast<const uint2*>(curw + r * 64 + 16 * (kk ^ ((r >> 1) & 3)) + 8 * (lane >> 5));
-          fb[j] = i8x8_to_f16x8(q.x, q.y);
-        } else {
-          fb[j] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, c));
-        }
+  // fragment f of sub-step kk (16 of the stage's 64 k): f < TN is the B
+  // fragment of column block f, then the A fragments of row blocks f - TN
+  auto ld1 = [&](const f16* cur, int kk, int f, f16x8* fa, f16x8* fb) {
+    const int c = kk * 2 + (lane >> 5);
+    if (f < TN) {
+      const int r = wn * WN + f * 32 + (lane & 31);
+      if constexpr (W8) {
+        const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
+        const uint2 q = *reinterpret_cast<const uint2*>(curw + r * 64 + 16 * (kk ^ ((r >> 1) & 3)) + 8 * (lane >> 5));
+        fb[f] = i8x8_to_f16x8(q.x, q.y);
+      } else {
+        fb[f] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, c));
       }
+    } else {
+      fa[f - TN] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + (f - TN) * 32 + (lane & 31), c));
+    }
+  };
+  // One k-step on stage `cur`: the next sub-step's fragment reads are
+  // interleaved one per R MFMAs with this sub-step's MFMAs.
+  auto kstep = [&](const f16* cur) {
+    constexpr int NF = TM + TN;
+    f16x8 af[2][TM], bf[2][TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + i * 32 + (lane & 31), c));
-    };
-    ld(0, af[0], bf[0]);
+    for (int f = 0; f < NF; ++f) ld1(cur, 0, f, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) ld(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) ld1(cur, kk + 1, f, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][i], bf[kk & 1][j], acc[i][j], 0, 0, 0);
     }
-    // schedule: step-0 fragments, then per step the next step's fragments
-    // interleaved one read per R MFMAs with this step's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      constexpr int R = (TM * TN) / (TM + TN) > 0 ? (TM * TN) / (TM + TN) : 1;
+      constexpr int R = (TM * TN) / NF > 0 ? (TM * TN) / NF : 1;
       if (kk + 1 < 4) {
 #pragma unroll
-        for (int q = 0; q < TM + TN; ++q) {
+        for (int q = 0; q < NF; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
         }
-        if (TM * TN > R * (TM + TN)) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * (TM + TN), 0);
+        if (TM * TN > R * NF) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * NF, 0);
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
       }
+    }
+  };
+
+  const int kt0 = split * a.kt_per_split;
+  const int kt1 = min(K / BK, kt0 + a.kt_per_split);
+  if constexpr (VG) {
+    // Register-staged copies, two stages of registers over two LDS stages:
+    // k-step kt computes on LDS stage kt % 2 while the loads of kt + 2 are in
+    // flight into one register set and the other set (k-step kt + 1, loaded
+    // a step earlier) is written to LDS stage (kt + 1) % 2 at its end.
+    static_assert(NS == 2, "register staging: two LDS stages");
+    i32x4 r0[LPW], r1[LPW];
+    auto gload = [&](int kt, i32x4* r) {
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int t = 0; t < LPW; ++t) {
+        if (t < TA_) r[t] = *reinterpret_cast<const i32x4*>(A + src_off[t] + k0);
+        else if constexpr (W8) r[t] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(W8p + src_off[t] + k0));
+        else r[t] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(Wf + src_off[t] + k0));
+      }
+    };
+    auto lput = [&](f16* st, const i32x4* r) {
+#pragma unroll
+      for (int t = 0; t < LPW; ++t)
+        *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(st) + (wave + NW * t) * 1024 + 16 * lane) = r[t];
+    };
+    if (kt0 < kt1) {
+      gload(kt0, r0);
+      if (kt0 + 1 < kt1) gload(kt0 + 1, r1);
+      lput(smem, r0);
+    }
+    lds_barrier();
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      // even step: LDS stage 0 holds kt, r1 holds kt + 1
+      if (kt + 2 < kt1) gload(kt + 2, r0);
+      // (always true: the block boundary keeps the register copies out of
+      // the MFMA region; without it the int8 tiles run out of registers)
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave < NW) kstep(smem);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < kt1) lput(smem + STAGE, r1);
+      lds_barrier();
+      if (kt + 1 >= kt1) break;
+      // odd step: LDS stage 1 holds kt + 1, r0 holds kt + 2
+      if (kt + 3 < kt1) gload(kt + 3, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave < NW) kstep(smem + STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 2 < kt1) lput(smem, r0);
+      lds_barrier();
+    }
+  } else {
+    // stages kt0 .. kt0 + NS - 2 in flight before the first k-step
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+      if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int rel = kt - kt0;
+      f16* cur = smem + (rel % NS) * STAGE;
+      f16* nxt = smem + ((rel + NS - 1) % NS) * STAGE;  // the stage read in step kt - 1
+      // wait for this wave's DMA of stage kt; the newer stages stay in flight
+      const int newer = min(NS - 2, kt1 - 1 - kt);
+      if (newer <= 0) PHI_WAIT_VMCNT(0);
+      else if (newer == 1) PHI_WAIT_VMCNT(LPW);
+      else PHI_WAIT_VMCNT(2 * LPW);
+      lds_barrier();
+      if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
+      kstep(cur);
     }
   }
 
