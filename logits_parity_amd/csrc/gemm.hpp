@@ -139,8 +139,13 @@ struct TileCfg {
   static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
 };
 
-template <class C, bool W8, int EPI, int NS>
-__global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
+// HW > 0 adds HW copy waves to the workgroup: they issue every global -> LDS
+// copy of the tile and take part in the k-step barriers, while the C::NW
+// compute waves only read fragments and run MFMAs.  A direct-to-LDS load
+// holds its wave at issue until the copy path takes it (tens of cycles
+// each), so copies issued by the compute waves leave their MFMA pipes idle.
+template <class C, bool W8, int EPI, int NS, int HW = 0>
+__global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs a) {
   // int8 weights take the register-staged copy (measured faster for their
   // 64-byte rows); binary16 operands go global -> LDS by DMA
   constexpr bool VG = W8;
@@ -155,8 +160,10 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   constexpr int STAGE = (BM * BK * 2 + BN * BK * WB) / 2;  // f16 elements per LDS stage
   constexpr int INS_A = BM * 8 / 64;                 // 1 KB DMA instructions for A per stage
   constexpr int INS_W = BN * BK * WB / 1024;
-  constexpr int LPW = (INS_A + INS_W) / NW;          // DMA instructions per wave per stage
-  static_assert(LPW * NW == INS_A + INS_W, "stage split");
+  static_assert(HW == 0 || !VG, "copy waves only on the DMA path");
+  constexpr int NDW = HW > 0 ? HW : NW;               // waves that issue the copies
+  constexpr int LPW = (INS_A + INS_W) / NDW;         // DMA instructions per copying wave per stage
+  static_assert(LPW * NDW == INS_A + INS_W, "stage split");
   static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
   static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
   constexpr int HD = EPI == EPI_QKV ? WN : 96;
@@ -183,7 +190,9 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   const int tn = rem / gm;
   const int m0 = tm * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const bool copies = HW == 0 || wave >= NW;            // this wave issues copies
+  const int dw = HW > 0 ? (copies ? wave - NW : 0) : wave;  // its index among the copying waves
+  const int wm = min(wave, NW - 1) / C::WGN, wn = min(wave, NW - 1) % C::WGN;
   const int K = a.K;
   const f16* A = reinterpret_cast<const f16*>(a.A);
 
@@ -193,12 +202,12 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
   // swizzled chunk of one row
   // A stage's first INS_A instructions are A rows, the rest W rows; with
   // INS_A a multiple of NW, instruction t of every wave is of one kind.
-  static_assert(INS_A % NW == 0, "A / W split of the DMA instructions");
-  constexpr int TA_ = INS_A / NW;  // instructions t < TA_ load A
+  static_assert(INS_A % NDW == 0, "A / W split of the DMA instructions");
+  constexpr int TA_ = INS_A / NDW;  // instructions t < TA_ load A
   int src_off[LPW > 0 ? LPW : 1];
 #pragma unroll
   for (int t = 0; t < LPW; ++t) {
-    const int j = wave + NW * t;
+    const int j = dw + NDW * t;
     const int s = j * 64 + lane;
     const bool is_w = t >= TA_;
     if (!is_w) {
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
-      const int j = wave + NW * t;
+      const int j = dw + NDW * t;
       lds_ptr_t dst = (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024);
       // weights are streamed once per tile row: non-temporal, so that they do
       // not push the activation tiles (re-read by every N-tile) out of L2
@@ -338,25 +347,36 @@ __global__ __launch_bounds__(C::NT) void phi_gemm_mfma_kernel(GemmArgs a) {
     }
   } else {
     // stages kt0 .. kt0 + NS - 2 in flight before the first k-step
+    if (copies) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-      if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
+      for (int i = 0; i < NS - 1; ++i)
+        if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
+    }
     for (int kt = kt0; kt < kt1; ++kt) {
       const int rel = kt - kt0;
       f16* cur = smem + (rel % NS) * STAGE;
       f16* nxt = smem + ((rel + NS - 1) % NS) * STAGE;  // the stage read in step kt - 1
-      // wait for this wave's DMA of stage kt; the newer stages stay in flight
-      const int newer = min(NS - 2, kt1 - 1 - kt);
-      if (newer <= 0) PHI_WAIT_VMCNT(0);
-      else if (newer == 1) PHI_WAIT_VMCNT(LPW);
-      else PHI_WAIT_VMCNT(2 * LPW);
+      if (copies) {
+        // wait for this wave's DMA of stage kt; the newer stages stay in flight
+        const int newer = min(NS - 2, kt1 - 1 - kt);
+        if (newer <= 0) PHI_WAIT_VMCNT(0);
+        else if (newer == 1) PHI_WAIT_VMCNT(LPW);
+        else PHI_WAIT_VMCNT(2 * LPW);
+      }
       lds_barrier();
-      if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
+      if (copies) {
+        if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
+        if (HW > 0) continue;
+      }
       kstep(cur);
     }
   }
 
   // ---------------------------------------------------------------- epilogue
+  if (HW > 0 && wave >= NW) {
+    if constexpr (EPI == EPI_QKV) __syncthreads();  // the one barrier of the QKV epilogue
+    return;
+  }
   const int grp = lane >> 5, col_l = lane & 31;
   auto row_of = [&](int i, int v) { return m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3); };
   float sc[TN];
