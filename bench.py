@@ -144,7 +144,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mini_f16_1x512")
-    ap.add_argument("--cpu-positions", type=int, default=256)
+    ap.add_argument("--cpu-positions", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,

@@ -71,7 +71,10 @@ def test_gemm_f32_tiny_shapes(phi, M, N, K):
 
 
 @pytest.mark.parametrize("wtype,M,I,K", [("f16", 512, 8192, 3072), ("f16", 77, 1024, 384),
-                                         ("i8", 300, 8192, 3072), ("f32", 40, 1024, 384)])
+                                         ("i8", 300, 8192, 3072), ("f32", 40, 1024, 384),
+                                         # 256x256 tiles (1024 tokens and more) with a ragged last M-tile:
+                                         # binary16 by direct-to-LDS copies, int8 register-staged
+                                         ("f16", 1100, 2048, 1024), ("i8", 1100, 2048, 1024)])
 def test_gate_up_silu_epilogue(phi, wtype, M, I, K):
     _say(f"gate_up silu {wtype} M={M} I={I} K={K}")
     adt = np.float32 if wtype == "f32" else np.float16
