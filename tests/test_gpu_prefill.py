@@ -106,6 +106,20 @@ def test_tiny_errors_are_reported(phi):
     assert e.value.status == 5  # PHI_E_WORKSPACE
 
 
+def test_mini_one_layer_ragged_1100_vs_oracle(phi):
+    """Full Phi-3-mini width, one layer, 1100 tokens: the 1024-token-and-up
+    GEMM tiles (QKV 256 x 192, gate/up and lm_head 256 x 256) with a ragged
+    last M-tile of 76 rows, against the live oracle."""
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.MINI, n_layers=1)
+    _say("mini 1 layer 1x1100")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 1, 1100)
+    got = _run(phi, cfg, to_device(ws, 1, "cuda"), ids)
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    _gate(got, ref)
+
+
 # ---------------------------------------------------------------- full shapes
 def _golden(name):
     path = os.path.join(GOLDEN, name + ".npz")
