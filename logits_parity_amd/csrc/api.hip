@@ -274,6 +274,17 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
 // Workgroups of the shared-key-block attention at which it beats the split
 // kernel (measured: 448 and more win at head_dim 64 to 128, 256 lose).
 constexpr long kAttnSharedMinWorkgroups = 384;
+#ifndef PHI_ATT8
+#define PHI_ATT8 1
+#endif
+#ifndef PHI_ATT8_MIN
+#define PHI_ATT8_MIN 256
+#endif
+constexpr long kAttnShared8MinWorkgroups = PHI_ATT8_MIN;
+#ifndef PHI_ATT8_MIN_S
+#define PHI_ATT8_MIN_S 2048
+#endif
+constexpr int kAttnShared8MinSeq = PHI_ATT8_MIN_S;
 
 phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
   a.scale_log2 = kLog2e / sqrtf((float)hd);
@@ -285,6 +296,13 @@ phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
   // workgroups to fill the chip at two per CU; split keys (32 queries per
   // workgroup, four times the workgroups) below that.
   const int heads = a.nh * batch;
+  if (PHI_ATT8 && a.S >= kAttnShared8MinSeq && (long)heads * ((a.S + 255) / 256) >= kAttnShared8MinWorkgroups) {
+    const dim3 grid(heads, (a.S + 255) / 256);
+    if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<128, 8>), grid, dim3(512), 0, st, a);
+    else if (hd == 64) hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<64, 8>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<96, 8>), grid, dim3(512), 0, st, a);
+    return launched();
+  }
   if ((long)heads * ((a.S + 127) / 128) >= kAttnSharedMinWorkgroups) {
     const dim3 grid(heads, (a.S + 127) / 128);
     if (hd == 128) hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<128>, grid, dim3(256), 0, st, a);
@@ -301,8 +319,18 @@ phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
 
 template <class ET, class AT>
 phi_status norm(bool embed, NormArgs a, hipStream_t st) {
-  if (embed) hipLaunchKernelGGL((phi_norm_kernel<ET, AT, true>), dim3(a.T), dim3(kNormThreads), 0, st, a);
-  else hipLaunchKernelGGL((phi_norm_kernel<ET, AT, false>), dim3(a.T), dim3(kNormThreads), 0, st, a);
+  // chunks per thread: hidden <= kNormMaxChunks * 1024 is checked at load
+  switch ((a.H + 4 * kNormThreads - 1) / (4 * kNormThreads)) {
+#define PHI_NORM_CASE(CH)                                                                                      \
+  case CH:                                                                                                     \
+    if (embed) hipLaunchKernelGGL((phi_norm_kernel<ET, AT, true, CH>), dim3(a.T), dim3(kNormThreads), 0, st, a); \
+    else hipLaunchKernelGGL((phi_norm_kernel<ET, AT, false, CH>), dim3(a.T), dim3(kNormThreads), 0, st, a);      \
+    break;
+    PHI_NORM_CASE(1) PHI_NORM_CASE(2) PHI_NORM_CASE(3) PHI_NORM_CASE(4)
+    PHI_NORM_CASE(5) PHI_NORM_CASE(6) PHI_NORM_CASE(7) PHI_NORM_CASE(8)
+#undef PHI_NORM_CASE
+    default: return PHI_E_SHAPE;
+  }
   return launched();
 }
 

@@ -250,31 +250,35 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
 // that makes the 32 rows of a fragment read conflict free); a V^T row is 8
 // slots with chunk' = chunk ^ ((d >> 1) & 7).  The MFMA formulation and the
 // key-row permutation are those of the split-key kernel.
-template <int D>
-__global__ __launch_bounds__(256, 2) void phi_attn_prefill_lds_kernel(AttnArgs a) {
+template <int D, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 96 || D == 128, "head_dim");
+  static_assert(NWV == 4 || NWV == 8, "waves per workgroup");
   constexpr int KB = 64, KS = D / 16, DB = D / 32;
-  constexpr int NSTG = D == 128 ? 2 : 3;                 // stages (2 workgroups per CU in LDS)
+  constexpr int QPW = 32 * NWV;                          // queries per workgroup
+  constexpr int HW = NWV / 2;                            // waves copying keys (the rest copy V^T)
+  // stages: 4 waves keep two workgroups per CU in LDS; 8 waves run one
+  constexpr int NSTG = (D == 128 && NWV == 4) ? 2 : 3;
   constexpr int PD = NSTG - 1;                           // blocks in flight ahead of the one read
   constexpr int KSLOT = D / 8 + 1;                       // 16-byte slots per LDS key row
   constexpr int NK = KB * KSLOT / 64, NV = D * 8 / 64;   // 1 KB DMA instructions per block
-  constexpr int NI = NK + NV, LPW = ((NK > NV ? NK : NV) + 1) / 2;  // loads per wave and block
+  constexpr int NI = NK + NV, LPW = ((NK > NV ? NK : NV) + HW - 1) / HW;  // loads per wave and block
   constexpr int STG = NI * 1024;                          // bytes per stage
   constexpr int OLD = D + 8;                              // output staging row (f16)
   static_assert(NK * 64 == KB * KSLOT, "key slots fill whole instructions");
-  static_assert(4 * 32 * OLD * 2 <= NSTG * STG, "output staging fits");
-  static_assert(2 * NSTG * STG <= 160 * 1024, "two workgroups per CU");
+  static_assert(NWV * 32 * OLD * 2 <= NSTG * STG, "output staging fits");
+  static_assert((8 / NWV) * NSTG * STG <= 160 * 1024, "workgroups per CU fit in LDS");
   __shared__ __attribute__((aligned(1024))) char lds[NSTG * STG];
 
-  const int qb = gridDim.y - 1 - blockIdx.y;   // 128-query block, longest first over the whole grid
+  const int qb = gridDim.y - 1 - blockIdx.y;   // query block, longest first over the whole grid
   const int h = blockIdx.x % a.nh, b = blockIdx.x / a.nh;
   const int g = h / (a.nh / a.nkv);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 5, col = lane & 31;
   const int S = a.S;
-  const int q0 = qb * 128 + 32 * w;            // this wave's first query
+  const int q0 = qb * QPW + 32 * w;            // this wave's first query
   const int qi = q0 + col;
-  const int last_q = min(qb * 128 + 127, S - 1);
+  const int last_q = min(qb * QPW + QPW - 1, S - 1);
   const int nb = last_q / KB + 1;              // key blocks of the workgroup
   const int wave_last = q0 < S ? min(q0 + 31, S - 1) : -1;  // -1: the wave has no queries
 
@@ -282,16 +286,16 @@ __global__ __launch_bounds__(256, 2) void phi_attn_prefill_lds_kernel(AttnArgs a
   const f16* Kp = reinterpret_cast<const f16*>(a.k) + ((size_t)(b * a.nkv + g) * S) * D;
   const f16* Vt = reinterpret_cast<const f16*>(a.vt) + ((size_t)(b * a.nkv + g) * D) * a.s_pad;
 
-  // DMA work: waves 0 and 1 copy the key rows (instructions 0 .. NK - 1,
-  // alternating), waves 2 and 3 the V^T rows (NK .. NI - 1); a wave with
+  // DMA work: the first HW waves copy the key rows (instructions 0 .. NK - 1,
+  // round robin), the other HW waves the V^T rows (NK .. NI - 1); a wave with
   // fewer instructions than LPW repeats its last one, so every wave has LPW
   // loads in flight per block and one vmcnt count fits all.
-  const bool kwave = w < 2;
-  const int nown = kwave ? NK : NV, wi = w & 1;
+  const bool kwave = w < HW;
+  const int nown = kwave ? NK : NV, wi = w % HW;
   int lrow[LPW], loff[LPW], ldst[LPW];
 #pragma unroll
   for (int t = 0; t < LPW; ++t) {
-    const int jj = min(wi + 2 * t, nown - 1 - ((nown - 1 - wi) & 1));  // index among the wave's kind
+    const int jj = min(wi + HW * t, nown - 1 - (nown - 1 - wi) % HW);  // index among the wave's kind
     const int sl = jj * 64 + lane;
     if (kwave) {
       const int r = sl / KSLOT, c = min(sl - r * KSLOT, D / 8 - 1);  // the padding slot re-reads the last chunk
