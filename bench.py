@@ -10,8 +10,9 @@ in HBM before the timed region.  Printed as one JSON line:
                 timed steps, bracketed by device synchronisation)
   roofline      the dominant kernel (fused gate/up GEMM + SiLU*up): its
                 launches inside forwards run right after the timed steps,
-                timed by HIP events the library records around each launch
-                on the forward's stream; algorithmic flops 2 * T * 2I * H per
+                timed by HIP events that the library attaches to each of its
+                dispatches on the forward's stream (the kernel's own run
+                time, as a kernel trace measures it); algorithmic flops 2 * T * 2I * H per
                 launch against the f16 MFMA peak; HBM traffic per launch from
                 the committed counter summary (null if the kernel changed)
   decode        K16/V8 decode attention per call at the two Phi-4 shapes,
@@ -61,7 +62,7 @@ def prefill_flops(cfg, batch, seq) -> float:
 
 def profile_forwards(model, ids, logits, workspace, stream, n):
     """Per-stage device time over n forwards, from HIP events that the library
-    records around each of its launches on the forward's stream."""
+    attaches to each of its kernel dispatches on the forward's stream."""
     model.profile_enable(True)
     for _ in range(n):
         model.prefill_logits(ids, logits, workspace, stream)

@@ -146,9 +146,12 @@ void phi_free(phi_model* m);
 const char* phi_strerror(int32_t status);
 
 /* ---- per-stage device timing of phi_prefill_logits ------------------------
- * Off by default.  When enabled, every kernel launch of phi_prefill_logits is
- * bracketed by two HIP events on the call's stream, so a stage's time is the
- * device time of its own launches inside real forwards.  phi_profile_read
+ * Off by default.  When enabled, every stage of phi_prefill_logits gets two
+ * HIP events on the call's stream.  A stage of one kernel passes them to that
+ * kernel's dispatch (hipExtLaunchKernelGGL), so they time the kernel itself,
+ * as a kernel trace does; the QKV stage with a KV cache (two launches) records
+ * them around both.  A stage's time is the device time of its own launches
+ * inside real forwards.  phi_profile_read
  * waits for the recorded events, writes per-stage total milliseconds and
  * launch counts (arrays of PHI_PROF_N), and clears the record.  Events are
  * created on the first enabled call; at most 16 forwards may be recorded

@@ -1,5 +1,6 @@
 // C ABI of libphi: argument checks, workspace planning and the stream-ordered
 // launch sequence of the prefill forward and of the decode attention.
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -149,33 +150,42 @@ constexpr int gemm_copy_waves() {
   return (!W8 && EPI != EPI_QKV && C::NW == 4 && C::TM * C::TN <= 8) ? 4 : 0;
 }
 
+// Kernel launch.  With profiling events (ev non-null) the two events ride on
+// the dispatch itself (hipExtLaunchKernelGGL), so their elapsed time is the
+// kernel's own run time, as a kernel trace reports it; otherwise a plain launch.
+#define PHI_LAUNCH(ev, kernel, grid, block, st, ...)                                                \
+  do {                                                                                              \
+    if (ev) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, (ev)[0], (ev)[1], 0, __VA_ARGS__);   \
+    else hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__);                              \
+  } while (0)
+
 template <class C, bool W8, int EPI>
-void launch_mfma(GemmArgs a, hipStream_t st) {
+void launch_mfma(GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
   const int units = a.tiles_m * a.tiles_n * a.splits;
   const int grid = (units + 7) / 8 * 8;
   constexpr int HW = gemm_copy_waves<C, W8, EPI>();
-  hipLaunchKernelGGL((phi_gemm_mfma_kernel<C, W8, EPI, gemm_stages<C, W8>(), HW>), dim3(grid), dim3(C::NT + 64 * HW),
-                     0, st, a);
+  PHI_LAUNCH(ev, (phi_gemm_mfma_kernel<C, W8, EPI, gemm_stages<C, W8>(), HW>), dim3(grid), dim3(C::NT + 64 * HW), st,
+             a);
 }
 
 template <bool W8, int EPI>
-void launch_cfg(int cfg, GemmArgs a, hipStream_t st) {
+void launch_cfg(int cfg, GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
   using QL = std::conditional_t<W8, CfgQL, CfgQL8>;
   using QS = std::conditional_t<W8, CfgQS, CfgQS8>;
   if constexpr (EPI == EPI_QKV) {
-    if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st);
-    else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st);
-    else if (cfg == C_Q64) launch_mfma<CfgQ64, W8, EPI>(a, st);
-    else launch_mfma<QS, W8, EPI>(a, st);
+    if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
+    else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st, ev);
+    else if (cfg == C_Q64) launch_mfma<CfgQ64, W8, EPI>(a, st, ev);
+    else launch_mfma<QS, W8, EPI>(a, st, ev);
   } else if constexpr (EPI == EPI_SILU) {
-    if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st);
-    else launch_mfma<CfgM, W8, EPI>(a, st);
+    if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st, ev);
+    else launch_mfma<CfgM, W8, EPI>(a, st, ev);
   } else if constexpr (EPI == EPI_F32) {
-    launch_mfma<CfgL, W8, EPI>(a, st);
+    launch_mfma<CfgL, W8, EPI>(a, st, ev);
   } else {
-    if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st);
-    else if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st);
-    else launch_mfma<CfgS, W8, EPI>(a, st);
+    if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st, ev);
+    else if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
+    else launch_mfma<CfgS, W8, EPI>(a, st, ev);
   }
 }
 
@@ -241,7 +251,8 @@ struct SimtCfg<EPI_QKV> { static constexpr int BN = 96; };
 // Runs one GEMM; returns the number of K splits whose partials the caller
 // must reduce (0 when the epilogue completed the result).
 template <int EPI>
-phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* partials = nullptr) {
+phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* partials = nullptr,
+                const hipEvent_t* ev = nullptr) {
   if (partials) *partials = 0;
   if (wtype == PHI_WT_F32) {
     constexpr int BN = SimtCfg<EPI>::BN;
@@ -249,7 +260,7 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
     a.tiles_n = EPI == EPI_SILU ? (a.N / 2) / (BN / 2) : (a.N + BN - 1) / BN;
     a.splits = 1;
     const int tiles = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((phi_gemm_simt_f32_kernel<BN, EPI>), dim3(tiles), dim3(256), 0, st, a);
+    PHI_LAUNCH(ev, (phi_gemm_simt_f32_kernel<BN, EPI>), dim3(tiles), dim3(256), st, a);
     return launched();
   }
   a.tiles_m = p.tiles_m;
@@ -261,13 +272,13 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
   if constexpr (EPI == EPI_RESID) {
     if (p.splits > 1) {
       if (partials) *partials = p.splits;
-      if (w8) launch_cfg<true, EPI_PARTIAL>(p.cfg, a, st);
-      else launch_cfg<false, EPI_PARTIAL>(p.cfg, a, st);
+      if (w8) launch_cfg<true, EPI_PARTIAL>(p.cfg, a, st, ev);
+      else launch_cfg<false, EPI_PARTIAL>(p.cfg, a, st, ev);
       return launched();
     }
   }
-  if (w8) launch_cfg<true, EPI>(p.cfg, a, st);
-  else launch_cfg<false, EPI>(p.cfg, a, st);
+  if (w8) launch_cfg<true, EPI>(p.cfg, a, st, ev);
+  else launch_cfg<false, EPI>(p.cfg, a, st, ev);
   return launched();
 }
 
@@ -286,10 +297,10 @@ constexpr long kAttnShared8MinWorkgroups = PHI_ATT8_MIN;
 #endif
 constexpr int kAttnShared8MinSeq = PHI_ATT8_MIN_S;
 
-phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
+phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st, const hipEvent_t* ev = nullptr) {
   a.scale_log2 = kLog2e / sqrtf((float)hd);
   if (f32) {
-    hipLaunchKernelGGL(phi_attn_prefill_f32_kernel, dim3((a.S + 63) / 64, a.nh, batch), dim3(64), 0, st, a);
+    PHI_LAUNCH(ev, (phi_attn_prefill_f32_kernel), dim3((a.S + 63) / 64, a.nh, batch), dim3(64), st, a);
     return launched();
   }
   // Shared key blocks (128 queries per workgroup) once there are enough
@@ -298,33 +309,33 @@ phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st) {
   const int heads = a.nh * batch;
   if (PHI_ATT8 && a.S >= kAttnShared8MinSeq && (long)heads * ((a.S + 255) / 256) >= kAttnShared8MinWorkgroups) {
     const dim3 grid(heads, (a.S + 255) / 256);
-    if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<128, 8>), grid, dim3(512), 0, st, a);
-    else if (hd == 64) hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<64, 8>), grid, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((phi_attn_prefill_lds_kernel<96, 8>), grid, dim3(512), 0, st, a);
+    if (hd == 128) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<128, 8>), grid, dim3(512), st, a);
+    else if (hd == 64) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<64, 8>), grid, dim3(512), st, a);
+    else PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<96, 8>), grid, dim3(512), st, a);
     return launched();
   }
   if ((long)heads * ((a.S + 127) / 128) >= kAttnSharedMinWorkgroups) {
     const dim3 grid(heads, (a.S + 127) / 128);
-    if (hd == 128) hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<128>, grid, dim3(256), 0, st, a);
-    else if (hd == 64) hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<64>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(phi_attn_prefill_lds_kernel<96>, grid, dim3(256), 0, st, a);
+    if (hd == 128) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<128>), grid, dim3(256), st, a);
+    else if (hd == 64) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<64>), grid, dim3(256), st, a);
+    else PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<96>), grid, dim3(256), st, a);
     return launched();
   }
   const dim3 grid(heads, (a.S + 31) / 32);
-  if (hd == 128) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<128, 4>), grid, dim3(256), 0, st, a);
-  else if (hd == 64) hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<64, 4>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((phi_attn_prefill_f16_kernel<96, 4>), grid, dim3(256), 0, st, a);
+  if (hd == 128) PHI_LAUNCH(ev, (phi_attn_prefill_f16_kernel<128, 4>), grid, dim3(256), st, a);
+  else if (hd == 64) PHI_LAUNCH(ev, (phi_attn_prefill_f16_kernel<64, 4>), grid, dim3(256), st, a);
+  else PHI_LAUNCH(ev, (phi_attn_prefill_f16_kernel<96, 4>), grid, dim3(256), st, a);
   return launched();
 }
 
 template <class ET, class AT>
-phi_status norm(bool embed, NormArgs a, hipStream_t st) {
+phi_status norm(bool embed, NormArgs a, hipStream_t st, const hipEvent_t* ev = nullptr) {
   // chunks per thread: hidden <= kNormMaxChunks * 1024 is checked at load
   switch ((a.H + 4 * kNormThreads - 1) / (4 * kNormThreads)) {
 #define PHI_NORM_CASE(CH)                                                                                      \
   case CH:                                                                                                     \
-    if (embed) hipLaunchKernelGGL((phi_norm_kernel<ET, AT, true, CH>), dim3(a.T), dim3(kNormThreads), 0, st, a); \
-    else hipLaunchKernelGGL((phi_norm_kernel<ET, AT, false, CH>), dim3(a.T), dim3(kNormThreads), 0, st, a);      \
+    if (embed) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, true, CH>), dim3(a.T), dim3(kNormThreads), st, a);       \
+    else PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH>), dim3(a.T), dim3(kNormThreads), st, a);            \
     break;
     PHI_NORM_CASE(1) PHI_NORM_CASE(2) PHI_NORM_CASE(3) PHI_NORM_CASE(4)
     PHI_NORM_CASE(5) PHI_NORM_CASE(6) PHI_NORM_CASE(7) PHI_NORM_CASE(8)
@@ -349,6 +360,15 @@ struct StageTimer {
   }
   void end() {
     if (on) (void)hipEventRecord(p->ev[2 * slot + 1], st);
+  }
+  // A stage of one kernel: its events go to the dispatch (PHI_LAUNCH) and
+  // time the kernel alone; nullptr when profiling is off.
+  const hipEvent_t* dispatch(int stage) {
+    on = false;
+    if (!p->enabled) return nullptr;
+    slot = p->used++;
+    p->stage[slot] = stage;
+    return &p->ev[2 * slot];
   }
 };
 
@@ -401,9 +421,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   na.V = c.vocab;
   na.eps = c.rms_eps;
   na.gain = m->layers[0].ln1;
-  tm.begin(PHI_PROF_EMBED);
-  phi_status s = norm<AT, AT>(true, na, st);
-  tm.end();
+  phi_status s = norm<AT, AT>(true, na, st, tm.dispatch(PHI_PROF_EMBED));
   if (s) return s;
 
   GemmArgs base{};
@@ -439,15 +457,17 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.k = const_cast<void*>(aa.k);
     g.vt = const_cast<void*>(aa.vt);
     g.bias = reinterpret_cast<const f16*>(L.qkv_bias);
-    tm.begin(PHI_PROF_QKV);
-    s = gemm<EPI_QKV>(wt, g, p.qkv, st);
-    if (!s && cache) s = kv_fill(cache, l, aa.k, aa.vt, batch, seq, p.s_pad, c.n_kv_heads, st);
-    tm.end();
+    if (cache) {  // the stage also fills the cache: events around both launches
+      tm.begin(PHI_PROF_QKV);
+      s = gemm<EPI_QKV>(wt, g, p.qkv, st);
+      if (!s) s = kv_fill(cache, l, aa.k, aa.vt, batch, seq, p.s_pad, c.n_kv_heads, st);
+      tm.end();
+    } else {
+      s = gemm<EPI_QKV>(wt, g, p.qkv, st, nullptr, tm.dispatch(PHI_PROF_QKV));
+    }
     if (s) return s;
 
-    tm.begin(PHI_PROF_ATTN);
-    s = attention(wt == PHI_WT_F32, aa, batch, hd, st);
-    tm.end();
+    s = attention(wt == PHI_WT_F32, aa, batch, hd, st, tm.dispatch(PHI_PROF_ATTN));
     if (s) return s;
 
     g = base;
@@ -459,15 +479,11 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.x = x;
     g.ldx = H;
     g.out = part;
-    tm.begin(PHI_PROF_O);
-    s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit);
-    tm.end();
+    s = gemm<EPI_RESID>(wt, g, p.o, st, &na.nsplit, tm.dispatch(PHI_PROF_O));
     if (s) return s;
 
     na.gain = L.ln2;
-    tm.begin(PHI_PROF_NORM);
-    s = norm<AT, AT>(false, na, st);
-    tm.end();
+    s = norm<AT, AT>(false, na, st, tm.dispatch(PHI_PROF_NORM));
     if (s) return s;
 
     g = base;
@@ -478,9 +494,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.K = H;
     g.act = act;
     g.ld_act = I;
-    tm.begin(PHI_PROF_GATE_UP);
-    s = gemm<EPI_SILU>(wt, g, p.gu, st);
-    tm.end();
+    s = gemm<EPI_SILU>(wt, g, p.gu, st, nullptr, tm.dispatch(PHI_PROF_GATE_UP));
     if (s) return s;
 
     g = base;
@@ -492,15 +506,11 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
     g.x = x;
     g.ldx = H;
     g.out = part;
-    tm.begin(PHI_PROF_DOWN);
-    s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit);
-    tm.end();
+    s = gemm<EPI_RESID>(wt, g, p.down, st, &na.nsplit, tm.dispatch(PHI_PROF_DOWN));
     if (s) return s;
 
     na.gain = l + 1 < c.n_layers ? m->layers[l + 1].ln1 : m->final_norm;
-    tm.begin(PHI_PROF_NORM);
-    s = norm<AT, AT>(false, na, st);
-    tm.end();
+    s = norm<AT, AT>(false, na, st, tm.dispatch(PHI_PROF_NORM));
     if (s) return s;
   }
 
@@ -512,10 +522,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   g.K = H;
   g.out = logits;
   g.ldo = c.vocab;
-  tm.begin(PHI_PROF_LM_HEAD);
-  s = gemm<EPI_F32>(wt, g, p.lm, st);
-  tm.end();
-  return s;
+  return gemm<EPI_F32>(wt, g, p.lm, st, nullptr, tm.dispatch(PHI_PROF_LM_HEAD));
 }
 
 // ---------------------------------------------------------------- decode plan
