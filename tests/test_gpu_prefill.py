@@ -70,6 +70,32 @@ def test_tiny_low_precision_vs_oracle(phi, wtype):
     _gate(got, prefill.prefill_logits(cfg, ws, ids))
 
 
+def test_tiny_f16_prompt_of_max_pos_tokens(phi):
+    # the longest prompt a model takes: positions up to max_pos - 1, the last
+    # row of the RoPE tables (ragged against every tile and key block)
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.TINY, wtype="f16", max_pos=300)
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 1, cfg.max_pos)
+    got = _run(phi, cfg, to_device(ws, cfg.n_layers), ids)
+    _gate(got, prefill.prefill_logits(cfg, ws, ids))
+
+
+def test_empty_prefill_is_refused_before_any_launch(phi):
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.TINY, wtype="f16")
+    m = phi.phi_load_fused(cfg, to_device(synth.WeightSet(cfg), cfg.n_layers))
+    L = phi.lib()
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    p = buf.data_ptr()
+    assert L.phi_prefill_logits(m.handle, p, 0, 8, p, p, 1 << 20, None) == 2  # PHI_E_SHAPE
+    assert L.phi_prefill_logits(m.handle, p, 1, 0, p, p, 1 << 20, None) == 2
+    assert L.phi_workspace_bytes(m.handle, 0, 8) == 0
+    assert L.phi_workspace_bytes(m.handle, 1, 0) == 0
+    torch.cuda.synchronize()
+    assert int(buf.sum()) == 0  # nothing was written
+
+
 def test_tiny_f32_gqa_unit_gains(phi):
     # harder regime: unit norm gains, GQA grouping
     from logits_parity_amd.weights import to_device
