@@ -49,16 +49,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // final merge).  Stage layout: keys [16 tokens][128 dims] binary16 with the
 // 16-byte chunk c of token row r stored at slot c ^ r (conflict-free
 // fragment reads), then the value codes [16][128] as in the page.
-template <int G, int NST>
-__global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a) {
+template <int G, int NST, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(DecodeArgs a) {
   constexpr int D = 128, PG = 16;
   constexpr int KBY = PG * D * 2, VBY = PG * D, SB = KBY + VBY, WB = NST * SB;
   constexpr int LPP = KBY / 1024 + VBY / 1024;  // loads per page and wave
   static_assert(G >= 1 && G <= 8, "GQA group");
   static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPP <= 63, "ring depth");
-  static_assert(4 * G * D * 4 + 4 * G * 2 * 4 <= 4 * WB, "merge staging fits in the rings");
-  __shared__ __attribute__((aligned(1024))) char lds[4 * WB];
-  __shared__ int s_err[4];
+  static_assert(NWV == 4 || NWV == 8, "waves per workgroup");
+  static_assert(NWV * G * D * 4 + NWV * G * 2 * 4 <= NWV * WB, "merge staging fits in the rings");
+  __shared__ __attribute__((aligned(1024))) char lds[NWV * WB];
+  __shared__ int s_err[NWV];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
   const int np = err ? 0 : (L + PG - 1) / PG;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(np, p_begin + a.pages_per_split);
-  int nw = p_end - p_begin - w > 0 ? (p_end - p_begin - w + 3) / 4 : 0;  // <= 64 (host: pages_per_split <= 256)
+  // pages of this wave: w, w + NWV, ... of the split (<= 64: the host keeps pages_per_split <= 64 NWV)
+  int nw = p_end - p_begin - w > 0 ? (p_end - p_begin - w + NWV - 1) / NWV : 0;
 
   // query operand: head hl (zero beyond the group), dims 32 k + 8 kq .. +7;
   // loaded together with the block-table entries, so both cost one latency
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
     for (int k = 0; k < 4; ++k) qf[k] = *reinterpret_cast<const f16x8*>(qrow + 32 * k);
   }
   // physical page of the wave's page i in lane i (lanes past nw re-read an entry in the row)
-  const int ti = min(p_begin + w + 4 * min(lane, max(nw - 1, 0)), a.max_pages - 1);
+  const int ti = min(p_begin + w + NWV * min(lane, max(nw - 1, 0)), a.max_pages - 1);
   int my_phys = a.block_table[(size_t)b * a.max_pages + ti];
   if (lane < nw && (my_phys < 0 || my_phys >= a.n_pages)) err = true;
   if (__any(err)) {  // the split's result becomes NaN; read nothing
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
     asm volatile("" ::: "memory");  // the page's LDS reads stay after the wait
     if (i + NST - 1 < nw) issue(i + NST - 1);  // into the stage of page i - 1, whose reads are done
     const char* st = ring + (i % NST) * SB;
-    const int pg = p_begin + w + 4 * i;
+    const int pg = p_begin + w + NWV * i;
 
     // 1. scores of the page's 16 tokens for heads hl: lane l holds tokens 4 kq + j
     f32x4 sc = f32x4{};
@@ -207,8 +209,8 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   __syncthreads();  // every wave is done with its ring: reuse it for the merge
-  float* s_o = reinterpret_cast<float*>(lds);            // [4][G][D]
-  float* s_ml = s_o + 4 * G * D;                           // [4][G][2]
+  float* s_o = reinterpret_cast<float*>(lds);            // [NWV][G][D]
+  float* s_ml = s_o + NWV * G * D;                         // [NWV][G][2]
   if (hl < G) {
 #pragma unroll
     for (int db = 0; db < 8; ++db)
@@ -221,15 +223,17 @@ __global__ __launch_bounds__(256, 2) void phi_decode_stream_kernel(DecodeArgs a)
   }
   if (lane == 0) s_err[w] = err;
   __syncthreads();
-  const bool bad = s_err[0] | s_err[1] | s_err[2] | s_err[3];
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  bool bad = false;
+#pragma unroll
+  for (int ww = 0; ww < NWV; ++ww) bad |= s_err[ww] != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NWV) {
     const int h = idx / D, d = idx - h * D;
     float mn = -__builtin_inff();
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mn = fmaxf(mn, s_ml[(ww * G + h) * 2]);
+    for (int ww = 0; ww < NWV; ++ww) mn = fmaxf(mn, s_ml[(ww * G + h) * 2]);
     float ls = 0.f, os = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NWV; ++ww) {
       const float mw = s_ml[(ww * G + h) * 2];
       const float f = mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - mn);
       ls += s_ml[(ww * G + h) * 2 + 1] * f;

@@ -76,6 +76,22 @@ def test_decode_long_splits_ragged(phi, max_ctx):
     assert rel.max() <= 2e-3, rel.max()
 
 
+# 16 sequences x 8 KV heads (128 workgroups) at max_ctx 4000 (250 pages)
+# would take four 64-page splits and the merge; they run as one split per
+# sequence on 8-wave workgroups instead.  Ragged lengths leave some waves
+# with no pages at all (a 1-token sequence has one page, for wave 0).
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_single_split_eight_waves_ragged(phi, G):
+    wl = synth.DecodeWorkload("t", batch=16, ctx=4000, n_q_heads=8 * G, n_kv_heads=8)
+    lens = [1, 16, 17, 100, 112, 113, 128, 129, 1000, 2047, 2048, 2049, 3333, 3999, 4000, 4000]
+    _say(f"decode one split, 8 waves, G={G}")
+    d = synth.decode_inputs(wl, ctx_lens=lens)
+    got = _gpu(phi, d, max_ctx=4000)
+    rel = _rel(got, _ref(d))
+    _say(f"  max rel L2 = {rel.max():.2e}")
+    assert rel.max() <= 2e-3, rel.max()
+
+
 def test_decode_page_permutation_is_invisible(phi):
     wl = synth.DecodeWorkload("t", batch=4, ctx=500, n_q_heads=8, n_kv_heads=2)
     d = synth.decode_inputs(wl)
