@@ -3,7 +3,8 @@
 //
 // Split kernel: a workgroup owns one (sequence, KV head, context split) and
 // serves all G query heads of the GQA group from one read of each K/V page.
-// Wave w takes pages w, w + 4, ... of the split and streams them through its
+// Its NWV waves (4, or 8 for one long split per sequence): wave w takes pages
+// w, w + NWV, ... of the split and streams them through its
 // own LDS ring by direct global -> LDS loads (no VGPR staging), so page
 // reads stay in flight while it computes.  Per page a wave
 //  1. forms the scores S^T[token][head] = K Q^T with v_mfma_f32_16x16x32_f16:
@@ -17,7 +18,7 @@
 //     l % 16), rounded to binary16; the V^T operand is built from 8 bytes of
 //     E4M3 per token (dims 8 (l % 16) .. +7 of the lane's 4 tokens), transposed
 //     bytewise by v_perm_b32 and widened exactly to binary16.
-// At the end the 4 waves are merged by log-sum-exp through LDS, and the split's
+// At the end the waves are merged by log-sum-exp through LDS, and the split's
 // (o unnormalised, max, sum) go to the workspace; with a single split the
 // kernel normalises and writes the output itself.  The per-head value scale
 // multiplies the final output once.
