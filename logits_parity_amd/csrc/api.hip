@@ -541,7 +541,9 @@ struct DecodePlan {
 // 16 x 8192 tokens 94.2-95.6 -> 88.7 us (160 workgroups of 512 pages).
 // One split per sequence on 8-wave workgroups replaces a multi-split plan
 // when the context fits one split (<= 512 pages: 64 per wave) and the
-// (sequence, KV head) pairs fill at least half the CUs.
+// (sequence, KV head) pairs fill at least half the CUs.  Measured at 40/10
+// heads: 16 x 4096 51-53 -> 47-48 us, 24 x 8192 132-134 -> 130 us; below the
+// cut the split plan wins (12 x 8192: 72 against 82 us, 8 x 8192: 53 against 77).
 constexpr long kDecode8MinUnits = 128;
 DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
   DecodePlan p;
