@@ -55,14 +55,13 @@ phi_status launched() { return hipGetLastError() == hipSuccess ? PHI_OK : PHI_E_
 using CfgL = TileCfg<256, 256, 2, 4>;
 using CfgM = TileCfg<256, 128, 2, 2>;   // wave tile 128 x 64
 using CfgS = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64
-// 256 x 192 and 128 x 192 tiles: binary16 runs 8 waves (wave tiles 64 x 96
-// and 32 x 96, still one head per wave for the QKV epilogue), twice the waves
-// issuing the tile's copies (4096 tokens: o_proj 4.21 -> 3.36 ms, down 7.87 ->
-// 7.05 ms, QKV 8.60 -> 8.08 ms per forward; 512 tokens: QKV 1.75 -> 1.64 ms);
-// int8 keeps 4 (its register-staged copy does not split over 8 waves)
-using CfgQL = TileCfg<256, 192, 2, 2>;   // wave tile 128 x 96 (one head per wave)
+// 256 x 192 and 128 x 192 tiles run 8 waves (wave tiles 64 x 96 and 32 x 96,
+// still one head per wave for the QKV epilogue): twice the waves issuing the
+// tile's copies.  binary16 at 4096 tokens: o_proj 4.21 -> 3.36 ms, down
+// 7.87 -> 7.05 ms, QKV 8.60 -> 8.08 ms per forward; 512 tokens: QKV 1.75 ->
+// 1.64 ms.  int8 at 4 x 1024 (register-staged copies, 44 per stage padded to
+// 6 per wave): o_proj 4.34 -> 3.62 ms, down 8.48 -> 7.83 ms.
 using CfgQL8 = TileCfg<256, 192, 4, 2>;  // 8 waves, wave tile 64 x 96
-using CfgQS = TileCfg<128, 192, 2, 2>;   // wave tile 64 x 96
 using CfgQS8 = TileCfg<128, 192, 4, 2>;  // 8 waves, wave tile 32 x 96
 using CfgQ128 = TileCfg<128, 256, 2, 2>;  // wave tile 64 x 128 (one 128-wide head per wave)
 using CfgQ64 = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64 (one 64-wide head per wave)
@@ -170,8 +169,8 @@ void launch_mfma(GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
 
 template <bool W8, int EPI>
 void launch_cfg(int cfg, GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
-  using QL = std::conditional_t<W8, CfgQL, CfgQL8>;
-  using QS = std::conditional_t<W8, CfgQS, CfgQS8>;
+  using QL = CfgQL8;
+  using QS = CfgQS8;
   if constexpr (EPI == EPI_QKV) {
     if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
     else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st, ev);

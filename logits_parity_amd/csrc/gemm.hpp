@@ -162,8 +162,13 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   constexpr int INS_W = BN * BK * WB / 1024;
   static_assert(HW == 0 || !VG, "copy waves only on the DMA path");
   constexpr int NDW = HW > 0 ? HW : NW;               // waves that issue the copies
-  constexpr int LPW = (INS_A + INS_W) / NDW;         // DMA instructions per copying wave per stage
-  static_assert(LPW * NDW == INS_A + INS_W, "stage split");
+  // copies per copying wave and stage; where they do not divide evenly (int8
+  // weights on 8 waves: 44 per stage) the surplus ones repeat the last copy,
+  // writing the same bytes to the same LDS slot
+  constexpr int LPW = (INS_A + INS_W + NDW - 1) / NDW;
+  constexpr bool PAD = LPW * NDW != INS_A + INS_W;
+  constexpr int JMAX = INS_A + INS_W - 1;             // last copy of a stage
+  static_assert(LPW * NDW == INS_A + INS_W || VG, "stage split (binary16 DMA tiles divide evenly)");
   static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
   static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
   constexpr int HD = EPI == EPI_QKV ? WN : 96;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   int src_off[LPW > 0 ? LPW : 1];
 #pragma unroll
   for (int t = 0; t < LPW; ++t) {
-    const int j = dw + NDW * t;
+    const int j = PAD ? min(dw + NDW * t, JMAX) : dw + NDW * t;
     const int s = j * 64 + lane;
     const bool is_w = t >= TA_;
     if (!is_w) {
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     const int k0 = kt * BK;
 #pragma unroll
     for (int t = 0; t < LPW; ++t) {
-      const int j = dw + NDW * t;
+      const int j = PAD ? min(dw + NDW * t, JMAX) : dw + NDW * t;
       lds_ptr_t dst = (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024);
       // weights are streamed once per tile row: non-temporal, so that they do
       // not push the activation tiles (re-read by every N-tile) out of L2
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     auto lput = [&](f16* st, const i32x4* r) {
 #pragma unroll
       for (int t = 0; t < LPW; ++t)
-        *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(st) + (wave + NW * t) * 1024 + 16 * lane) = r[t];
+        *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(st) + (PAD ? min(wave + NW * t, JMAX) : wave + NW * t) * 1024 + 16 * lane) = r[t];
     };
     if (kt0 < kt1) {
       gload(kt0, r0);
