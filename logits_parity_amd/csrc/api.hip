@@ -140,13 +140,16 @@ constexpr int gemm_stages() {
 }
 
 // Copy waves (4 extra waves that issue all global -> LDS copies) for the
-// binary16 tiles of at most 8 MFMA blocks per wave: measured 5% faster on the
-// gate/up and residual GEMMs at 512 tokens.  Not for the larger tiles (they
-// need all 512 registers per lane of one wave) nor the QKV epilogue (its RoPE
-// factors spill at 256 registers per lane).
+// binary16 4-wave tiles of at most 8 MFMA blocks per wave: measured 5% faster
+// on the gate/up and residual GEMMs at 512 tokens.  And for the 8-wave
+// 128 x 192 QKV tile (144 registers, so 12 waves fit): QKV at 512 tokens
+// 1.595 -> 1.49 ms per forward.  Not for the 4-wave QKV tiles (their RoPE
+// factors spill at 256 registers per lane), nor the other 8-wave tiles (the
+// 256 x 192 residual tile spills at 168 registers and measured 19% slower).
 template <class C, bool W8, int EPI>
 constexpr int gemm_copy_waves() {
-  return (!W8 && EPI != EPI_QKV && C::NW == 4 && C::TM * C::TN <= 8) ? 4 : 0;
+  return ((!W8 && EPI != EPI_QKV && C::NW == 4 && C::TM * C::TN <= 8) ||
+          (!W8 && EPI == EPI_QKV && C::NW == 8 && C::BM == 128 && C::WN == 96)) ? 4 : 0;
 }
 
 // Kernel launch.  With profiling events (ev non-null) the two events ride on
