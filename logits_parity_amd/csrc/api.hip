@@ -71,13 +71,10 @@ struct GemmPlan {
   int cfg, tiles_m, tiles_n, splits, kpt, group_m;
 };
 
-#ifndef PHI_GEMM_GROUP_M
-#define PHI_GEMM_GROUP_M 8
-#endif
 // M-tiles per tile group when there are more M-tiles than that: the 32
 // workgroups that run together on an XCD then cover a block of 8 x 4 tiles
 // (12 distinct A and W tiles in its L2) instead of a column of all M-tiles.
-constexpr int kGemmGroupM = PHI_GEMM_GROUP_M;
+constexpr int kGemmGroupM = 8;
 
 constexpr int kCUs = 256;
 
@@ -287,17 +284,12 @@ phi_status gemm(int wtype, GemmArgs a, const GemmPlan& p, hipStream_t st, int* p
 // Workgroups of the shared-key-block attention at which it beats the split
 // kernel (measured: 448 and more win at head_dim 64 to 128, 256 lose).
 constexpr long kAttnSharedMinWorkgroups = 384;
-#ifndef PHI_ATT8
-#define PHI_ATT8 1
-#endif
-#ifndef PHI_ATT8_MIN
-#define PHI_ATT8_MIN 256
-#endif
-constexpr long kAttnShared8MinWorkgroups = PHI_ATT8_MIN;
-#ifndef PHI_ATT8_MIN_S
-#define PHI_ATT8_MIN_S 2048
-#endif
-constexpr int kAttnShared8MinSeq = PHI_ATT8_MIN_S;
+// The shared-key-block kernel on 8 waves (256 queries per workgroup): from
+// S = 2048 with at least 256 workgroups.  At 1 x 4096: 4.75 -> 4.55-4.60 ms
+// of attention per forward; at 4 x 1024 the 4-wave form stays faster (a
+// 256-query block wastes more of the causal diagonal at short S).
+constexpr long kAttnShared8MinWorkgroups = 256;
+constexpr int kAttnShared8MinSeq = 2048;
 
 phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st, const hipEvent_t* ev = nullptr) {
   a.scale_log2 = kLog2e / sqrtf((float)hd);
@@ -309,7 +301,7 @@ phi_status attention(bool f32, AttnArgs a, int batch, int hd, hipStream_t st, co
   // workgroups to fill the chip at two per CU; split keys (32 queries per
   // workgroup, four times the workgroups) below that.
   const int heads = a.nh * batch;
-  if (PHI_ATT8 && a.S >= kAttnShared8MinSeq && (long)heads * ((a.S + 255) / 256) >= kAttnShared8MinWorkgroups) {
+  if (a.S >= kAttnShared8MinSeq && (long)heads * ((a.S + 255) / 256) >= kAttnShared8MinWorkgroups) {
     const dim3 grid(heads, (a.S + 255) / 256);
     if (hd == 128) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<128, 8>), grid, dim3(512), st, a);
     else if (hd == 64) PHI_LAUNCH(ev, (phi_attn_prefill_lds_kernel<64, 8>), grid, dim3(512), st, a);
