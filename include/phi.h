@@ -216,6 +216,9 @@ phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, 
  * Supported: D = 128, page_size = 16, n_q_heads / n_kv_heads <= 8 and
  * dividing.  The work is split over the context (split-KV); partial results
  * are combined by a log-sum-exp merge kernel ([P3], "attention and merge").
+ * When one split per sequence suffices (the context fits one split and the
+ * (sequence, KV head) pairs fill the GPU) the split kernel normalises the
+ * output itself and no merge runs; the workspace size follows the plan.
  * Device-side values are checked in the kernel: a ctx_len outside
  * [1, max_pages * 16] or a page id outside [0, n_pages) makes that
  * sequence's output NaN instead of reading outside the pool. */
