@@ -124,6 +124,28 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.phi_decode_workspace_bytes(None, 1, 16) == 0
 
 
+def test_decode_plan_split_counts():
+    # the decode workspace holds (o, max, sum) partials per (sequence, query
+    # head, split), so its size shows the split plan: one split per sequence
+    # (8-wave workgroups) where the context fits 512 pages and the (sequence,
+    # KV head) pairs number at least 128; the 4-wave split plan below that
+    L = phi.lib()
+    r = lambda x: (x + 255) // 256 * 256
+
+    def splits(B, ctx, hq=40, hkv=10):
+        got = L.attn_decode_k16v8_workspace_bytes(B, hq, hkv, 128, ctx)
+        found = [s for s in range(1, 65) if r(B * hq * s * 128 * 4) + r(B * hq * s * 2 * 4) == got]
+        assert len(found) == 1, (B, ctx, got)
+        return found[0]
+    assert splits(32, 1024) == 1    # 320 pairs: one 64-page split each, 4 waves
+    assert splits(16, 8192) == 1    # 160 pairs: one 512-page split each, 8 waves
+    assert splits(16, 4096) == 1
+    assert splits(24, 8192) == 1
+    assert splits(12, 8192) == 4    # 120 pairs: four 128-page splits and the merge
+    assert splits(8, 8192) == 4     # 80 pairs
+    assert splits(16, 16384) == 4   # 1024 pages do not fit one split
+
+
 def test_no_packed_fp32_instructions_in_device_code(tmp_path):
     """Device code is built with packed fp32 math disabled; check the ISA of
     this build for any v_pk_{add,mul,fma}_f32."""
