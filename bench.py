@@ -16,7 +16,9 @@ in HBM before the timed region.  Printed as one JSON line:
                 launch against the f16 MFMA peak; HBM traffic per launch from
                 the committed counter summary (null if the kernel changed)
   decode        K16/V8 decode attention per call at the two Phi-4 shapes,
-                algorithmic bytes per call against HBM bandwidth
+                algorithmic bytes per call against HBM bandwidth; HBM
+                traffic per call from the committed counter summary (null
+                if the kernel changed)
   cpu_baseline  the fp64 oracle on the host, on the first positions of the
                 same ids (a bounded sample), with the parity of those rows
 """
@@ -39,9 +41,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(profile: str, source: str):
-    """HBM-side bytes per launch from a committed counter summary, or None when
-    the kernel source has changed since the counters were taken."""
+def measured_traffic(profile: str, source: str, key: str = "traffic_bytes_per_launch"):
+    """HBM-side bytes per launch (the `key` line) from a committed counter
+    summary, or None when the kernel source has changed since the counters
+    were taken."""
     import hashlib
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
@@ -49,7 +52,7 @@ def measured_traffic(profile: str, source: str):
         digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
         if fields.get("kernel_source_sha256", "").strip() != digest:
             return None
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields[key])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -109,7 +112,9 @@ def time_decode(phi, torch, np, synth, wl, reps=200):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": wl.name, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_k16v8_traffic.md", "logits_parity_amd/csrc/decode.hpp",
+                                                     f"traffic_bytes_per_call_{wl.name}")},
             "cache_copies_rotated": copies}
 
 
