@@ -146,6 +146,21 @@ def test_mini_one_layer_ragged_1100_vs_oracle(phi):
     _gate(got, ref)
 
 
+def test_mini_w8_one_layer_ragged_1100_vs_oracle(phi):
+    """The same shape with int8 weights against the oracle on those weights:
+    the 8-wave 256 x 192 QKV tile (44 register-staged copies per stage padded
+    to 6 per wave) and the int8 256 x 256 gate/up and lm_head tiles, with a
+    ragged last M-tile."""
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.MINI_W8, n_layers=1)
+    _say("mini int8 1 layer 1x1100")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 1, 1100)
+    got = _run(phi, cfg, to_device(ws, 1, "cuda"), ids)
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    _gate(got, ref)
+
+
 # ---------------------------------------------------------------- full shapes
 def _golden(name):
     path = os.path.join(GOLDEN, name + ".npz")
