@@ -161,6 +161,23 @@ def test_mini_w8_one_layer_ragged_1100_vs_oracle(phi):
     _gate(got, ref)
 
 
+@pytest.mark.parametrize("wtype", ["f16", "i8"])
+def test_mini_one_layer_ragged_4000_vs_oracle(phi, wtype):
+    """One layer, 4000 tokens: the residual GEMMs take the 8-wave 256 x 192
+    tile (16 x 16 = 256 tiles; int8 with its register-staged copies padded)
+    with a last M-tile of 160 rows, and attention the 8-wave
+    shared-key-block kernel at a ragged S (the oracle takes about 40 s)."""
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.MINI if wtype == "f16" else synth.MINI_W8, n_layers=1)
+    _say(f"mini {wtype} 1 layer 1x4000")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, 1, 4000)
+    got = _run(phi, cfg, to_device(ws, 1, "cuda"), ids)
+    _say("  oracle")
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    _gate(got, ref)
+
+
 # ---------------------------------------------------------------- full shapes
 def _golden(name):
     path = os.path.join(GOLDEN, name + ".npz")
