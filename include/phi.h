@@ -219,9 +219,13 @@ phi_status phi_attention_prefill(int32_t act_f32, const void* q, const void* k, 
  * When one split per sequence suffices (the context fits one split and the
  * (sequence, KV head) pairs fill the GPU) the split kernel normalises the
  * output itself and no merge runs; the workspace size follows the plan.
+ * max_ctx is the longest context of the call (1 <= max_ctx <= max_pages *
+ * 16, PHI_E_RANGE otherwise): it sizes the split plan and the workspace, so
+ * the workspace query and the call must use the same value.
  * Device-side values are checked in the kernel: a ctx_len outside
- * [1, max_pages * 16] or a page id outside [0, n_pages) makes that
- * sequence's output NaN instead of reading outside the pool. */
+ * [1, max_ctx] or a page id outside [0, n_pages) makes that sequence's
+ * output NaN instead of reading outside the pool or dropping the pages past
+ * the plan. */
 size_t attn_decode_k16v8_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                          int32_t head_dim, int32_t max_ctx);
 phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
@@ -293,8 +297,9 @@ phi_status phi_prefill_fill_k16v8(const phi_model* m, const int32_t* ids, int32_
  * positions[b] + 1 for every b (1 <= max_ctx <= max_pages * 16 and
  * <= max_pos; PHI_E_RANGE otherwise).  Device-side values are checked in the
  * kernels: a position whose slot lies outside the table or pool is not
- * written, and a cache length outside [1, max_pages * 16] makes that
- * sequence's attention output NaN.  Workspace:
+ * written, and a position outside [0, max_ctx) makes that sequence's
+ * attention output, and so its logits, NaN (its RoPE position is then
+ * clamped into the table, which only affects that NaN row).  Workspace:
  * phi_decode_workspace_bytes(m, batch, max_ctx). */
 size_t phi_decode_workspace_bytes(const phi_model* m, int32_t batch, int32_t max_ctx);
 phi_status phi_decode_step_k16v8(const phi_model* m, const int32_t* ids, const int32_t* positions, int32_t batch,

@@ -13,7 +13,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libphi.so")
+# PHI_LIB names another build of the library (the host-sanitizer test uses it)
+LIB_PATH = os.environ.get("PHI_LIB") or os.path.join(HERE, "libphi.so")
 
 PHI_WT_F32, PHI_WT_F16, PHI_WT_I8 = 0, 1, 2
 PROF_STAGES = ("embed", "qkv", "attn", "o_proj", "norm", "gate_up", "down", "lm_head")

@@ -231,14 +231,24 @@ bool rows_fit(const phi_config& c, long long rows) {
   return rows >= 1 && rows * w < (1ll << 31) && rows * c.vocab < (1ll << 40);
 }
 
+// The GEMM kernels form operand offsets (row * K + column) in int32: every
+// weight's rows x K, and the activation rows x K of a call, must stay below 2^31.
+constexpr long long kMaxElems = 1ll << 31;
+inline bool elems_fit(long long rows, long long k) { return rows >= 1 && k >= 1 && rows * k < kMaxElems; }
+
 // head_dim 64 and 128 run on the MFMA paths only (binary16 and int8 weights).
+// Every product below is formed in 64 bits from fields bounded first.
 bool check_config(const phi_config* c) {
   const bool hd_ok = c->head_dim == 96 || ((c->head_dim == 64 || c->head_dim == 128) && c->wtype != PHI_WT_F32);
-  return c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && hd_ok &&
-         c->n_heads >= 1 && c->n_kv_heads >= 1 && c->n_heads % c->n_kv_heads == 0 &&
-         (c->n_heads * c->head_dim) % 64 == 0 && c->intermediate >= 128 && c->intermediate % 128 == 0 &&
-         c->hidden <= kNormMaxChunks * 4 * kNormThreads && c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 &&
-         c->max_pos <= kMaxPos;
+  if (!(c->n_layers >= 1 && c->hidden >= 64 && c->hidden % 64 == 0 && hd_ok && c->n_heads >= 1 &&
+        c->n_kv_heads >= 1 && c->n_heads <= (1 << 16) && c->n_heads % c->n_kv_heads == 0 &&
+        c->intermediate >= 128 && c->intermediate % 128 == 0 && c->hidden <= kNormMaxChunks * 4 * kNormThreads &&
+        c->vocab >= 4 && c->vocab % 4 == 0 && c->max_pos >= 1 && c->max_pos <= kMaxPos))
+    return false;
+  const long long H = c->hidden, hd = c->head_dim, I = c->intermediate;
+  const long long attn_w = (long long)c->n_heads * hd, qkv_rows = ((long long)c->n_heads + 2ll * c->n_kv_heads) * hd;
+  return attn_w % 64 == 0 && elems_fit(qkv_rows, H) && elems_fit(H, attn_w) && elems_fit(2 * I, H) &&
+         elems_fit(H, I) && elems_fit(c->vocab, H);
 }
 
 // ---------------------------------------------------------------- GEMM dispatch
@@ -568,8 +578,8 @@ DecodePlan plan_decode(int batch, int n_q_heads, int n_kv_heads, int max_ctx) {
 // Launch of split-KV decode attention + merge (arguments already checked).
 phi_status decode_attention(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
                             const int32_t* block_table, const int32_t* ctx_lens, int batch, int n_q_heads,
-                            int n_kv_heads, int n_pages, int max_pages, float sm_scale, void* out, void* workspace,
-                            const DecodePlan& p, hipStream_t st) {
+                            int n_kv_heads, int n_pages, int max_pages, int max_ctx, float sm_scale, void* out,
+                            void* workspace, const DecodePlan& p, hipStream_t st) {
   DecodeArgs a{};
   a.q = reinterpret_cast<const f16*>(q);
   a.k_pool = reinterpret_cast<const f16*>(k_pool);
@@ -587,6 +597,7 @@ phi_status decode_attention(const void* q, const void* k_pool, const void* v_poo
   a.max_pages = max_pages;
   a.n_split = p.n_split;
   a.pages_per_split = p.pages_per_split;
+  a.max_ctx = max_ctx;
   a.scale_log2 = sm_scale * kLog2e;
   const dim3 grid(p.n_split, n_kv_heads, batch);
   if (p.waves == 8) {
@@ -683,7 +694,7 @@ phi_status decode_step(const phi_model* m, const int32_t* ids, const int32_t* po
   int32_t* ctx = reinterpret_cast<int32_t*>(ws + p.off_ctx);
   const int wt = c.wtype;
 
-  hipLaunchKernelGGL(phi_ctx_from_pos_kernel, dim3((B + 255) / 256), dim3(256), 0, st, positions, ctx, B);
+  hipLaunchKernelGGL(phi_ctx_from_pos_kernel, dim3((B + 255) / 256), dim3(256), 0, st, positions, ctx, B, max_ctx);
   phi_status s = launched();
   if (s) return s;
 
@@ -731,8 +742,8 @@ phi_status decode_step(const phi_model* m, const int32_t* ids, const int32_t* po
                        cache->max_pages, cache->k_pools[l], cache->v_pools[l], st)))
       return s;
     if ((s = decode_attention(q, cache->k_pools[l], cache->v_pools[l], vs, cache->block_table, ctx, B, c.n_heads,
-                              c.n_kv_heads, cache->n_pages, cache->max_pages, sm_scale, attn, ws + p.off_att,
-                              p.att, st)))
+                              c.n_kv_heads, cache->n_pages, cache->max_pages, max_ctx, sm_scale, attn,
+                              ws + p.off_att, p.att, st)))
       return s;
 
     g = base;
@@ -797,6 +808,26 @@ phi_status check_cache(const phi_model* m, const phi_kv_cache* cache) {
   }
   return PHI_OK;
 }
+
+// Host checks shared by the decode-attention entry points; on success *plan
+// holds the split plan.
+phi_status check_decode_args(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
+                             const int32_t* block_table, const int32_t* ctx_lens, const void* out, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t n_pages, int32_t max_pages, int32_t max_ctx, float sm_scale, DecodePlan* plan) {
+  if (!q || !k_pool || !v_pool || !v_scale || !block_table || !ctx_lens || !out) return PHI_E_NULL;
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || head_dim != 128 ||
+      page_size != 16 || n_pages < 1 || max_pages < 1 || batch > (1 << 20) || n_q_heads > (1 << 12))
+    return PHI_E_SHAPE;
+  const int G = n_q_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PHI_E_SHAPE;
+  if (max_ctx < 1 || (long long)max_ctx > (long long)max_pages * page_size || !(sm_scale > 0.f)) return PHI_E_RANGE;
+  if ((long long)n_pages * n_kv_heads * 16 * 128 * 2 > (1ll << 40)) return PHI_E_SHAPE;
+  *plan = plan_decode(batch, n_q_heads, n_kv_heads, max_ctx);
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PHI_E_ALIGN;
+  return PHI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -941,6 +972,7 @@ phi_status phi_linear_f32out(int32_t wtype, const void* a, const void* w, const 
   if (wtype != PHI_WT_F32 && wtype != PHI_WT_F16 && wtype != PHI_WT_I8) return PHI_E_DTYPE;
   if ((wtype == PHI_WT_I8) != (scale != nullptr)) return PHI_E_NULL;
   if (M < 1 || N < 4 || K < 64 || K % 64 || N % 4) return PHI_E_SHAPE;
+  if (!elems_fit(M, K) || !elems_fit(N, K)) return PHI_E_SHAPE;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(scale)) return PHI_E_ALIGN;
   GemmArgs g{};
   g.A = a;
@@ -960,6 +992,7 @@ phi_status phi_gate_up_silu(int32_t wtype, const void* a, const void* w, const v
   if (wtype != PHI_WT_F32 && wtype != PHI_WT_F16 && wtype != PHI_WT_I8) return PHI_E_DTYPE;
   if ((wtype == PHI_WT_I8) != (scale != nullptr)) return PHI_E_NULL;
   if (M < 1 || I < 128 || K < 64 || K % 64 || I % 128) return PHI_E_SHAPE;
+  if (!elems_fit(M, K) || !elems_fit(2ll * I, K)) return PHI_E_SHAPE;
   if (!aligned16(a) || !aligned16(w) || !aligned16(act) || !aligned16(scale)) return PHI_E_ALIGN;
   GemmArgs g{};
   g.A = a;
@@ -1007,20 +1040,15 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
                              int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t n_pages,
                              int32_t max_pages, int32_t max_ctx, float sm_scale, void* out, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  if (!q || !k_pool || !v_pool || !v_scale || !block_table || !ctx_lens || !out || !workspace) return PHI_E_NULL;
-  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || head_dim != 128 ||
-      page_size != 16 || n_pages < 1 || max_pages < 1)
-    return PHI_E_SHAPE;
-  const int G = n_q_heads / n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PHI_E_SHAPE;
-  if (max_ctx < 1 || max_ctx > max_pages * page_size || !(sm_scale > 0.f)) return PHI_E_RANGE;
-  if ((long long)n_pages * n_kv_heads * 16 * 128 * 2 > (1ll << 40)) return PHI_E_SHAPE;
-  const DecodePlan p = plan_decode(batch, n_q_heads, n_kv_heads, max_ctx);
+  if (!workspace) return PHI_E_NULL;
+  DecodePlan p;
+  const phi_status s = check_decode_args(q, k_pool, v_pool, v_scale, block_table, ctx_lens, out, batch, n_q_heads,
+                                         n_kv_heads, head_dim, page_size, n_pages, max_pages, max_ctx, sm_scale, &p);
+  if (s) return s;
   if (workspace_bytes < p.total) return PHI_E_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) || !aligned16(workspace))
-    return PHI_E_ALIGN;
+  if (!aligned16(workspace)) return PHI_E_ALIGN;
   return decode_attention(q, k_pool, v_pool, v_scale, block_table, ctx_lens, batch, n_q_heads, n_kv_heads,
-                          n_pages, max_pages, sm_scale, out, workspace, p, as_stream(stream));
+                          n_pages, max_pages, max_ctx, sm_scale, out, workspace, p, as_stream(stream));
 }
 
 phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,

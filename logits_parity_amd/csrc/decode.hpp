@@ -40,6 +40,7 @@ struct DecodeArgs {
   float* part_ml;  // [B][Hq][n_split][2]
   f16* out;        // [B][Hq][128]
   int B, Hq, Hkv, n_pages, max_pages, n_split, pages_per_split;
+  int max_ctx;       // longest context the split plan covers (<= max_pages * 16)
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(De
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane & 15, kq = lane >> 4;  // score layout: head column, token quad
   const int L = a.ctx_lens[b];
-  bool err = L < 1 || L > a.max_pages * PG;
+  // a length beyond the plan's max_ctx would lose its trailing pages: NaN instead
+  bool err = L < 1 || L > a.max_ctx;
   const int np = err ? 0 : (L + PG - 1) / PG;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(np, p_begin + a.pages_per_split);
@@ -387,10 +389,14 @@ __global__ __launch_bounds__(256) void phi_kv_fill_kernel(KvFillArgs a) {
 }
 
 // ctx[b] = pos[b] + 1: the cache length a decode step attends over once its
-// token is appended.
-__global__ void phi_ctx_from_pos_kernel(const int32_t* pos, int32_t* ctx, int B) {
+// token is appended.  A position outside [0, max_ctx) gives length 0, which
+// the attention kernel turns into a NaN output for that sequence.
+__global__ void phi_ctx_from_pos_kernel(const int32_t* pos, int32_t* ctx, int B, int max_ctx) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) ctx[b] = pos[b] + 1;
+  if (b < B) {
+    const int p = pos[b];
+    ctx[b] = (p >= 0 && p < max_ctx) ? p + 1 : 0;
+  }
 }
 
 }  // namespace phi

@@ -113,21 +113,23 @@ def prefill_fill(cfg, weights, ids: np.ndarray, v_scale: np.ndarray, exact: bool
     return out, cache, raw
 
 
-_last_values: dict = {}   # layer -> unquantised value [kv_heads, d] of the last decode step
-
-
-def decode_step(cfg, weights, token: int, cache: SeqCache, v_scale: np.ndarray, exact: bool = False) -> np.ndarray:
+def decode_step(cfg, weights, token: int, cache: SeqCache, v_scale: np.ndarray, exact: bool = False,
+                return_values: bool = False):
     """One decode step of one sequence: the token at position cache.length()
     is appended to every layer's cache, then attends over all cached tokens.
-    Returns logits fp64 [vocab]; the cache grows by one token."""
+    Returns logits fp64 [vocab]; the cache grows by one token.  With
+    return_values, returns (logits, values) where values[l] is the step's
+    unquantised value [kv_heads, d] of layer l (what was encoded into the
+    cache)."""
     p = cache.length()
     x = widen(weights.embed[np.array([token])])
     nh, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
     group = nh // nkv
+    values = []
     for l in range(cfg.n_layers):
         lw = weights.layer(l)
         q, k, v = _qkv(x, lw, cfg, np.array([p]))  # q [1, heads, d]
-        _last_values[l] = v[0]
+        values.append(v[0])
         _store(cache.layers[l], k, v, v_scale[l], exact)
         if exact:
             K = np.stack([e[0] for e in cache.layers[l]])   # [p + 1, kv_heads, d]
@@ -146,7 +148,8 @@ def decode_step(cfg, weights, token: int, cache: SeqCache, v_scale: np.ndarray, 
             a = decode.decode_attention(q.astype(np.float64), kp, vp, v_scale[l], table,
                                         np.array([p + 1]), 1.0 / np.sqrt(hd))[0]
         x = _mlp_tail(x, a.reshape(1, -1), lw, cfg)
-    return linear(rms_norm(x, weights.final_norm, cfg.rms_eps), weights.lm_head)[0]
+    out = linear(rms_norm(x, weights.final_norm, cfg.rms_eps), weights.lm_head)[0]
+    return (out, values) if return_values else out
 
 
 def value_scales_from(raw_per_seq: list, n_layers: int) -> np.ndarray:

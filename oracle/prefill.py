@@ -107,8 +107,10 @@ def decoder_layer(x: np.ndarray, lw: dict, cfg, positions: np.ndarray) -> np.nda
     return x + linear(m, lw["down"])
 
 
-def prefill_logits(cfg, weights, ids: np.ndarray, n_layers: int | None = None) -> np.ndarray:
-    """Logits fp64 [B, S, vocab] for ids int [B, S].
+def final_hidden(cfg, weights, ids: np.ndarray, n_layers: int | None = None) -> np.ndarray:
+    """The normalised final hidden state rmsnorm(x) * g_final, fp64 [B, S, H],
+    that the untied lm_head multiplies: every step of the forward except the
+    last product.
 
     `weights` provides .embed, .layer(l) (dict: ln1, qkv, o, ln2, gate_up,
     down), .final_norm and .lm_head, each as stored.  Positions run 0..S-1 from
@@ -123,7 +125,20 @@ def prefill_logits(cfg, weights, ids: np.ndarray, n_layers: int | None = None) -
     for l in range(L):
         lw = weights.layer(l)
         xs = [decoder_layer(x, lw, cfg, pos) for x in xs]
-    out = np.empty((B, S, cfg.vocab), dtype=np.float64)
-    for b in range(B):
-        out[b] = linear(rms_norm(xs[b], weights.final_norm, cfg.rms_eps), weights.lm_head)
+    return np.stack([rms_norm(x, weights.final_norm, cfg.rms_eps) for x in xs])
+
+
+def logits_from_hidden(hidden: np.ndarray, lm_head) -> np.ndarray:
+    """The last step of the forward: logits = hidden W_lm^T, fp64 (untied
+    lm_head, P1 section 2, Methods table)."""
+    return linear(np.asarray(hidden, dtype=np.float64), lm_head)
+
+
+def prefill_logits(cfg, weights, ids: np.ndarray, n_layers: int | None = None) -> np.ndarray:
+    """Logits fp64 [B, S, vocab] for ids int [B, S]: final_hidden followed by
+    the lm_head product."""
+    h = final_hidden(cfg, weights, ids, n_layers)
+    out = np.empty(h.shape[:2] + (cfg.vocab,), dtype=np.float64)
+    for b in range(h.shape[0]):
+        out[b] = logits_from_hidden(h[b], weights.lm_head)
     return out

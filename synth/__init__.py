@@ -48,9 +48,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    # SYNTH_LIB names another build of synth.c (the host-sanitizer test uses it)
+    path = os.environ.get("SYNTH_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path):
+            build()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     u64, i64, i32, dbl, cs = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_char_p
     for nm in ("synth_normal_f64", "synth_normal_f32", "synth_normal_f16"):

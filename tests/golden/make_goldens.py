@@ -7,8 +7,15 @@ For each prefill workload it saves ``<workload>.npz`` holding
   argmax, gap                 oracle argmax and top-2 gap at every position
   pos, rows                   full oracle logit rows (float32) at sampled
                               positions, flat index b * seq + s
-and, for the int8 workload, the same fields for the float16 oracle on the
-float16 weights the int8 ones were quantized from (prefix ``f16_``).
+  hidden                      the oracle's normalised final hidden state
+                              rmsnorm(x) * g_final at every position, float32
+                              [batch * seq, hidden]: a test forms any logit
+                              row from it with the oracle's own lm_head step
+                              (oracle.prefill.logits_from_hidden).  Rounding
+                              it to float32 moves a row's cosine by about
+                              1e-14, far below the 1e-5 gate.
+and, for the int8 workload, argmax, gap, pos and rows for the float16 oracle
+on the float16 weights the int8 ones were quantized from (prefix ``f16_``).
 
 Usage:  python tests/golden/make_goldens.py [workload ...]
 """
@@ -38,15 +45,20 @@ def ids_digest(ids: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(ids, dtype=np.int32).tobytes()).hexdigest()
 
 
-def run(cfg, ids, pos):
+def run(cfg, ids, pos, keep_hidden=True):
     ws = synth.WeightSet(cfg, cache_layers=False)
     t = time.time()
-    logits = prefill.prefill_logits(cfg, ws, ids)
+    hidden = prefill.final_hidden(cfg, ws, ids).reshape(-1, cfg.hidden)
+    flat = prefill.logits_from_hidden(hidden, ws.lm_head)
     print(f"  oracle {cfg.name} {ids.shape}: {time.time() - t:.0f} s", flush=True)
-    flat = logits.reshape(-1, cfg.vocab)
     out = {"argmax": np.argmax(flat, axis=1).astype(np.int32), "gap": parity.top2_gap(flat),
            "rows": flat[pos].astype(np.float32)}
-    del logits, flat
+    if keep_hidden:
+        out["hidden"] = hidden.astype(np.float32)
+        # the stored (float32) hidden state reproduces the fp64 rows
+        again = prefill.logits_from_hidden(out["hidden"][pos], ws.lm_head)
+        print(f"  float32 hidden: min row cosine {parity.row_cosines(again, flat[pos]).min():.15f}", flush=True)
+    del hidden, flat
     out["weights_sha256"] = np.array(synth.WeightSet(cfg, cache_layers=False).digest())
     return out
 
@@ -58,7 +70,7 @@ def make(name: str):
     res = {"pos": pos, "ids_sha256": np.array(ids_digest(ids))}
     res.update(run(wl.cfg, ids, pos))
     if wl.cfg.wtype == "i8":
-        f16 = run(synth.as_f16_config(wl.cfg), ids, pos)
+        f16 = run(synth.as_f16_config(wl.cfg), ids, pos, keep_hidden=False)
         res.update({"f16_" + k: v for k, v in f16.items()})
     path = os.path.join(HERE, name + ".npz")
     np.savez_compressed(path, **res)

@@ -124,6 +124,23 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.phi_decode_workspace_bytes(None, 1, 16) == 0
 
 
+def test_int32_offset_guards_before_any_hip_call():
+    """The GEMM kernels form operand offsets in int32: a weight or activation
+    of 2^31 elements or more is refused on the host (PHI_E_SHAPE)."""
+    L = phi.lib()
+    # lm_head [V][H] just below 2^31 elements passes the shape checks (and stops
+    # at the misaligned state pointer, still before any HIP call)
+    assert _load(_cfg(hidden=8192, vocab=262144 - 4), state=0x1008) == 6
+    assert _load(_cfg(hidden=8192, vocab=262144)) == 2         # V * H = 2^31
+    assert _load(_cfg(hidden=4096, intermediate=262144)) == 2  # gate_up [2I][H] = 2^31
+    assert _load(_cfg(n_heads=1 << 20, n_kv_heads=1 << 20)) == 2   # head count bounded before any product
+    assert _load(_cfg(n_heads=(1 << 16) - 32, n_kv_heads=1)) == 2  # fused QKV rows x H past 2^31
+    assert L.phi_linear_f32out(1, 0x100, 0x200, None, 0x300, 1 << 25, 4, 64, None) == 2   # M * K = 2^31
+    assert L.phi_linear_f32out(1, 0x100, 0x200, None, 0x300, 4, 1 << 25, 64, None) == 2   # N * K = 2^31
+    assert L.phi_gate_up_silu(1, 0x100, 0x200, None, 0x300, 4, 1 << 24, 64, None) == 2    # 2 I * K = 2^31
+    assert L.phi_gate_up_silu(1, 0x100, 0x200, None, 0x300, 1 << 25, 128, 64, None) == 2  # M * K = 2^31
+
+
 def test_decode_plan_split_counts():
     # the decode workspace holds (o, max, sum) partials per (sequence, query
     # head, split), so its size shows the split plan: one split per sequence

@@ -5,11 +5,16 @@ then decode steps append one token per sequence and attend over the cache
 (phi_decode_step_k16v8).  The oracle is oracle/kv_chain.py.
 
 Gates:
-  - pools after the prefill: keys within one binary16 ulp of the oracle's
-    (the GPU rounds fp32 accumulators, the oracle fp64 values, to binary16)
-    and identical for >= 99 % of elements; value codes decode to within one
-    E4M3 step of the oracle's and are identical for >= 99 % of elements (a
-    value next to a rounding boundary may land on the neighbouring code);
+  - pools after the prefill and after the decode steps: keys within the
+    binary16 rounding of the oracle's key plus the error that the binary16
+    activations feeding the QKV GEMM carry into it (the GPU rounds fp32
+    accumulators, the oracle fp64 values, to binary16; the fraction of
+    identical keys is printed, not gated, since that activation error is of
+    the order of a binary16 step); decoded values within half an E4M3 step of
+    the oracle's unquantised value, widened by the same activation error; and
+    value codes identical to the oracle's for >= 95 % of elements (a value
+    within the activation error of an E4M3 rounding boundary may land on the
+    neighbouring code: about 2^-11 / 2^-4 of them, so about 99 % agree);
   - decode-step logits: cosine >= 0.99999 per sequence and argmax agreement
     where the oracle's top-2 gap exceeds 1e-3 (the prefill gate).
 """
@@ -124,9 +129,10 @@ def _chain(phi, cfg, lens, steps, seed):
         got = got.cpu().numpy()
         ref = []
         for b in range(len(lens)):
-            ref.append(kv_chain.decode_step(cfg, wo, int(ids[b]), oc[b], v_scale))
+            logits_b, vals = kv_chain.decode_step(cfg, wo, int(ids[b]), oc[b], v_scale, return_values=True)
+            ref.append(logits_b)
             for l in range(cfg.n_layers):   # the step's unquantised value, for the pool check
-                rv[b][l].append(kv_chain._last_values[l])
+                rv[b][l].append(vals[l])
         ref = np.stack(ref)
         s = parity.summary(got, ref)
         _say(f"  step {k}: min_cos={s['min_cos']:.9f} gated={s['gated']} agree={s['gated_agree']}")

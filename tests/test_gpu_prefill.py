@@ -7,8 +7,11 @@ logits).  The int8 path is gated against the oracle run on the int8 weights
 
 Small cases run the oracle live.  Full Phi-3-mini shapes compare with oracle
 results stored under tests/golden/ (written by make_goldens.py, which calls
-only the oracle): full rows at sampled positions plus argmax and top-2 gap at
-every position.  The input digests stored with them must match.
+only the oracle): the oracle's final normalised hidden state at every
+position, from which each reference logit row is formed here by the oracle's
+own lm_head step, so the cosine is gated at every position; argmax and top-2
+gap at every position; and full rows at sampled positions.  The input digests
+stored with them must match.
 """
 import hashlib
 import os
@@ -186,8 +189,24 @@ def _golden(name):
     return np.load(path)
 
 
-def _check_golden(g, got_flat, ids, digest, prefix=""):
-    """Oracle-trust first: the stored results must belong to these exact inputs."""
+def _all_position_cosines(g, got_flat, lm_head):
+    """Cosine at every position: each reference row is the oracle's lm_head
+    step on its stored final hidden state (float32-stored, moving a cosine by
+    about 1e-14)."""
+    hidden = g["hidden"]
+    assert hidden.shape[0] == got_flat.shape[0]
+    cos = np.empty(len(got_flat))
+    for r0 in range(0, len(got_flat), 512):
+        ref = prefill.logits_from_hidden(hidden[r0:r0 + 512], lm_head)
+        cos[r0:r0 + 512] = parity.row_cosines(got_flat[r0:r0 + 512], ref)
+    return cos
+
+
+def _check_golden(g, got_flat, ids, digest, prefix="", lm_head=None):
+    """Oracle-trust first: the stored results must belong to these exact
+    inputs.  Returns the cosines (at every position when the stored hidden
+    state and the lm_head are given, else at the sampled rows) and the
+    positions whose gated argmax disagrees."""
     assert str(g["ids_sha256"]) == hashlib.sha256(np.ascontiguousarray(ids, np.int32).tobytes()).hexdigest()
     assert str(g[prefix + "weights_sha256"]) == digest
     pos = g["pos"]
@@ -199,6 +218,13 @@ def _check_golden(g, got_flat, ids, digest, prefix=""):
     fails = np.nonzero(gated & ~agree)[0]
     _say(f"  sampled min_cos={cos.min():.9f} mean={cos.mean():.9f}; argmax gated={gated.sum()} "
          f"agree={(agree & gated).sum()} all-agree={agree.sum()}/{len(agree)}")
+    if lm_head is not None and not prefix:
+        full = _all_position_cosines(g, got_flat, lm_head)
+        # the sampled rows agree with the rows formed from the stored hidden state
+        assert np.abs(full[pos] - cos).max() < 1e-9
+        _say(f"  every position ({len(full)}): min_cos={full.min():.9f} mean={full.mean():.9f} "
+             f"worst at {int(np.argmin(full))}")
+        cos = full
     return cos, fails
 
 
@@ -215,7 +241,8 @@ def test_mini_f16_vs_stored_oracle(phi, mini_f16, mini_digest, name):
     ids = synth.token_ids(wl.cfg, wl.batch, wl.seq)
     got = _run(phi, wl.cfg, mini_f16[1], ids).reshape(-1, wl.cfg.vocab).astype(np.float64)
     assert np.all(np.isfinite(got))
-    cos, fails = _check_golden(g, got, ids, mini_digest)
+    cos, fails = _check_golden(g, got, ids, mini_digest, lm_head=mini_f16[0].lm_head)
+    assert len(cos) == wl.tokens
     assert cos.min() >= COS_GATE
     assert len(fails) == 0, fails[:20]
 
@@ -228,7 +255,8 @@ def test_mini_w8_vs_stored_oracle(phi, mini_w8, mini_digest):
     ids = synth.token_ids(wl.cfg, wl.batch, wl.seq)
     got = _run(phi, wl.cfg, mini_w8[1], ids).reshape(-1, wl.cfg.vocab).astype(np.float64)
     assert np.all(np.isfinite(got))
-    cos, fails = _check_golden(g, got, ids, mini_w8[0].digest())
+    cos, fails = _check_golden(g, got, ids, mini_w8[0].digest(), lm_head=mini_w8[0].lm_head)
+    assert len(cos) == wl.tokens
     assert cos.min() >= COS_GATE
     assert len(fails) == 0, fails[:20]
     # reported: distance to the float16 oracle is the quantisation's, not the kernel's
@@ -250,4 +278,6 @@ def test_mini_prefix_invariance_and_determinism(phi, mini_f16):
     # within fp32 rounding, same argmax wherever the top-2 gap exceeds 1e-3
     c = _run(phi, wl.cfg, mini_f16[1], ids[:, :200])
     s = parity.summary(c[0], a[0, :200])
+    _say(f"  200-token prefix vs the 512-token run: 1 - min_cos = {1 - s['min_cos']:.3e}, "
+         f"bitwise equal rows {int(np.all(c[0] == a[0, :200], axis=1).sum())}/200")
     assert s["min_cos"] > 1 - 1e-6 and not s["failures"], s
