@@ -234,6 +234,28 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
                              int32_t n_pages, int32_t max_pages, int32_t max_ctx, float sm_scale, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- decode attention without a workspace ---------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, checks, kernels and results as attn_decode_k16v8, without the
+ * workspace: the split partials go to a fixed scratch array inside the
+ * library, PHI_DECODE_SCRATCH_BYTES on each GPU the library runs on, held
+ * from the first call on that GPU until the process ends.  A call whose plan
+ * needs more (attn_decode_k16v8_workspace_bytes tells) returns
+ * PHI_E_WORKSPACE before any HIP call.  `stream` must belong to the current
+ * device (PHI_E_RANGE otherwise), whose scratch copy the call uses.  The call
+ * allocates nothing: no hipMalloc, no library allocation.  Every call on one
+ * GPU shares that GPU's scratch array, which keeps the last call's partials:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  Nothing needs clearing between
+ * calls: every partial a call reads is written earlier in the same call. */
+#define PHI_DECODE_SCRATCH_BYTES (16u << 20)
+phi_status attn_decode_k16v8_noalloc(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+                                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                     int32_t n_pages, int32_t max_pages, int32_t max_ctx, float sm_scale, void* out,
+                                     void* stream);
+
 /* ---- K16/V8 cache write ([P3]) --------------------------------------------
  * The step before decode attention: append one token per sequence to the
  * paged pool ([P3] names the write of the compressed cache in its

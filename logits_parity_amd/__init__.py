@@ -25,7 +25,7 @@ EXPORTS = ("phi_state_bytes", "phi_load_fused", "phi_workspace_bytes", "phi_pref
            "phi_strerror", "phi_linear_f32out", "phi_gate_up_silu", "phi_attention_vt_stride", "phi_attention_prefill",
            "attn_decode_k16v8_workspace_bytes", "attn_decode_k16v8", "phi_kv_pool_slots", "phi_profile_enable",
            "phi_profile_read", "kv_append_k16v8", "phi_prefill_fill_k16v8", "phi_decode_workspace_bytes",
-           "phi_decode_step_k16v8")
+           "phi_decode_step_k16v8", "attn_decode_k16v8_noalloc")
 
 
 class PhiError(RuntimeError):
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "phi_attention_prefill": (i32, [i32, P, P, P, P, i32, i32, i32, i32, i32, P]),
         "attn_decode_k16v8_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "attn_decode_k16v8": (i32, [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P, sz, P]),
+        "attn_decode_k16v8_noalloc": (i32, [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32, P, P]),
         "kv_append_k16v8": (i32, [P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]),
         "phi_prefill_fill_k16v8": (i32, [P, P, i32, i32, P, ctypes.POINTER(phi_kv_cache), P, sz, P]),
         "phi_decode_workspace_bytes": (sz, [P, i32, i32]),
@@ -325,6 +326,22 @@ def attn_decode_k16v8(q, k_pool, v_pool, v_scale, block_table, ctx_lens, max_ctx
                                    float(sm_scale), _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_decode_k16v8")
+    return out
+
+
+def attn_decode_k16v8_noalloc(q, k_pool, v_pool, v_scale, block_table, ctx_lens, max_ctx: int, sm_scale: float,
+                              out=None, stream=None):
+    """attn_decode_k16v8 with its partials in the library's fixed scratch array
+    (no workspace); see include/phi.h."""
+    import torch
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pool.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    _check(lib().attn_decode_k16v8_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(v_scale), _ptr(block_table),
+                                           _ptr(ctx_lens), B, Hq, Hkv, D, page, P, block_table.shape[1], max_ctx,
+                                           float(sm_scale), _ptr(out), _stream(stream)),
+           "attn_decode_k16v8_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -808,6 +809,34 @@ phi_status check_cache(const phi_model* m, const phi_kv_cache* cache) {
   }
   return PHI_OK;
 }
+}  // namespace
+
+// Split partials of attn_decode_k16v8_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: only its per-device address from
+// hipGetSymbolAddress (decode_scratch below) is ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) char scratch[PHI_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, resolved once per device
+// (with that device current) on its first use.
+phi_status decode_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PHI_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PHI_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PHI_OK;
+}
 
 // Host checks shared by the decode-attention entry points; on success *plan
 // holds the split plan.
@@ -1049,6 +1078,29 @@ phi_status attn_decode_k16v8(const void* q, const void* k_pool, const void* v_po
   if (!aligned16(workspace)) return PHI_E_ALIGN;
   return decode_attention(q, k_pool, v_pool, v_scale, block_table, ctx_lens, batch, n_q_heads, n_kv_heads,
                           n_pages, max_pages, max_ctx, sm_scale, out, workspace, p, as_stream(stream));
+}
+
+phi_status attn_decode_k16v8_noalloc(const void* q, const void* k_pool, const void* v_pool, const float* v_scale,
+                                     const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+                                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                     int32_t n_pages, int32_t max_pages, int32_t max_ctx, float sm_scale, void* out,
+                                     void* stream) {
+  DecodePlan p;
+  phi_status s = check_decode_args(q, k_pool, v_pool, v_scale, block_table, ctx_lens, out, batch, n_q_heads,
+                                   n_kv_heads, head_dim, page_size, n_pages, max_pages, max_ctx, sm_scale, &p);
+  if (s) return s;
+  if (p.total > (size_t)PHI_DECODE_SCRATCH_BYTES) return PHI_E_WORKSPACE;
+  // the stream must belong to the current device, whose scratch copy is used
+  hipStream_t st = as_stream(stream);
+  if (st) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(st, &sdev) != hipSuccess) return PHI_E_HIP;
+    if (cur != sdev) return PHI_E_RANGE;
+  }
+  void* ws = nullptr;
+  if ((s = decode_scratch(&ws))) return s;
+  return decode_attention(q, k_pool, v_pool, v_scale, block_table, ctx_lens, batch, n_q_heads, n_kv_heads,
+                          n_pages, max_pages, max_ctx, sm_scale, out, ws, p, st);
 }
 
 phi_status kv_append_k16v8(const void* k_new, const void* v_new, const float* v_scale, const int32_t* block_table,

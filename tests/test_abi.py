@@ -141,6 +141,27 @@ def test_int32_offset_guards_before_any_hip_call():
     assert L.phi_gate_up_silu(1, 0x100, 0x200, None, 0x300, 1 << 25, 128, 64, None) == 2  # M * K = 2^31
 
 
+def test_noalloc_decode_rejects_before_any_hip_call():
+    """attn_decode_k16v8_noalloc takes the checks of attn_decode_k16v8, and a
+    plan whose partials exceed the library's scratch array is refused with
+    PHI_E_WORKSPACE before anything is enqueued."""
+    L = phi.lib()
+    args = [0x100, 0x200, 0x300, 0x400, 0x500, 0x600]
+
+    def dec(batch=2, hq=8, hkv=2, d=128, page=16, n_pages=8, max_pages=4, max_ctx=64):
+        return L.attn_decode_k16v8_noalloc(*args, batch, hq, hkv, d, page, n_pages, max_pages, max_ctx, 0.1,
+                                           0x700, None)
+    assert L.attn_decode_k16v8_noalloc(None, *args[1:], 2, 8, 2, 128, 16, 8, 4, 64, 0.1, 0x700, None) == 1
+    assert dec(d=96) == 2
+    assert dec(hq=6, hkv=4) == 2
+    assert dec(max_ctx=65) == 4
+    limit = 16 << 20
+    need = L.attn_decode_k16v8_workspace_bytes(4096, 64, 8, 128, 100000)
+    assert need > limit
+    assert dec(batch=4096, hq=64, hkv=8, n_pages=1 << 20, max_pages=6250, max_ctx=100000) == 5
+    assert L.attn_decode_k16v8_workspace_bytes(3, 40, 10, 128, 3000) <= limit
+
+
 def test_decode_plan_split_counts():
     # the decode workspace holds (o, max, sum) partials per (sequence, query
     # head, split), so its size shows the split plan: one split per sequence
