@@ -54,7 +54,12 @@ phi_status launched() { return hipGetLastError() == hipSuccess ? PHI_OK : PHI_E_
 // a 4-wave 128 x 128 layout (gate/up at 4096 tokens 12.6 -> 12.1 ms per
 // forward, int8 13.3 -> 12.3 ms)
 using CfgL = TileCfg<256, 256, 2, 4>;
-using CfgM = TileCfg<256, 128, 2, 2>;   // wave tile 128 x 64
+// 8 compute waves of 64 x 64 (with 4 copy waves: 12 waves, 99 registers):
+// two compute waves per SIMD, so one issues MFMAs while the other waits on
+// LDS.  At 512 tokens, against 4 compute waves of 128 x 64: o_proj 0.585 ->
+// 0.527, down 1.029 -> 0.977, gate/up 1.723 -> 1.692 ms per forward; 8 copy
+// waves instead of 4 measured slower (0.544 / 1.018 / 1.712).
+using CfgM = TileCfg<256, 128, 4, 2>;
 using CfgS = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64
 // 256 x 192 and 128 x 192 tiles run 8 waves (wave tiles 64 x 96 and 32 x 96,
 // still one head per wave for the QKV epilogue): twice the waves issuing the
@@ -138,8 +143,9 @@ constexpr int gemm_stages() {
 }
 
 // Copy waves (4 extra waves that issue all global -> LDS copies) for the
-// binary16 4-wave tiles of at most 8 MFMA blocks per wave: measured 5% faster
-// on the gate/up and residual GEMMs at 512 tokens.  And for the 8-wave
+// binary16 4-wave tiles of at most 8 MFMA blocks per wave (measured 5% faster
+// on the gate/up and residual GEMMs at 512 tokens), the 8-wave 256 x 128
+// tile, and the 8-wave
 // 128 x 192 QKV tile (144 registers, so 12 waves fit): QKV at 512 tokens
 // 1.595 -> 1.49 ms per forward.  Not for the 4-wave QKV tiles (their RoPE
 // factors spill at 256 registers per lane), nor the other 8-wave tiles (the
@@ -147,6 +153,7 @@ constexpr int gemm_stages() {
 template <class C, bool W8, int EPI>
 constexpr int gemm_copy_waves() {
   return ((!W8 && EPI != EPI_QKV && C::NW == 4 && C::TM * C::TN <= 8) ||
+          (!W8 && EPI != EPI_QKV && C::BM == 256 && C::BN == 128 && C::NW == 8) ||
           (!W8 && EPI == EPI_QKV && C::NW == 8 && C::BM == 128 && C::WN == 96)) ? 4 : 0;
 }
 

@@ -1,8 +1,9 @@
 // Prefill GEMMs: y[M][N] = a[M][K] w[N][K]^T with fused epilogues.
 //
 // MFMA core (binary16 activations; binary16 or int8 weights):
-//  - 4 waves of 64 lanes, each owning a WM x WN sub-tile built from
-//    v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators.
+//  - 4 or 8 compute waves of 64 lanes, each owning a WM x WN sub-tile built
+//    from v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators, plus
+//    optional copy waves that only issue the global -> LDS copies.
 //  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
 //    them in flight while one is consumed, so the DMA of a k-step has NS - 1
 //    k-steps of MFMA work to arrive.  Operands go global -> LDS directly
@@ -16,8 +17,11 @@
 //    at one logical chunk touch 16 distinct 16-byte bank groups of the
 //    256-byte LDS bank row, so fragment reads are conflict free (int8 rows:
 //    chunk' = chunk ^ ((row >> 1) & 3) over their four chunks).
-//  - Each k-step's fragment reads for step s+1 are issued before the MFMAs of
-//    step s (scheduling barriers keep the compiler from re-serialising them).
+//  - Fragments are double-buffered over the four k16 sub-steps of a k-step:
+//    the reads for sub-step s + 1 are interleaved behind the MFMAs of
+//    sub-step s (scheduling barriers keep the compiler from re-serialising
+//    them).  The stage barrier of k-step kt + 1 sits before the last
+//    sub-step of kt, so the next stage's first reads also run under MFMAs.
 //  - Split-K: a launch may cut K into `splits` ranges; each writes an fp32
 //    partial tile that the next kernel (the residual + RMSNorm) reduces in a
 //    fixed order, so results do not depend on scheduling.
@@ -351,29 +355,76 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       lds_barrier();
     }
   } else {
-    // stages kt0 .. kt0 + NS - 2 in flight before the first k-step
-    if (copies) {
+    // The stage barrier of k-step kt + 1 sits before the last k16 sub-step
+    // of k-step kt: every fragment of stage kt is in registers by then, so
+    // the next stage's first fragment reads run under kt's last MFMAs instead
+    // of in front of the next k-step's first ones.  Barrier B(j) (stage j has
+    // landed, every read of stage j - 2 is done) lets the copying waves fill
+    // stage (j - 1) % NS with k-step j + NS - 1.
+    constexpr int NF = TM + TN;
+    constexpr int R = (TM * TN) / NF > 0 ? (TM * TN) / NF : 1;
+    auto wait_stage = [&](int j) {  // this wave's DMA of stage j; newer stages stay in flight
+      const int newer = min(NS - 2, kt1 - 1 - j);
+      if (newer <= 0) PHI_WAIT_VMCNT(0);
+      else if (newer == 1) PHI_WAIT_VMCNT(LPW);
+      else PHI_WAIT_VMCNT(2 * LPW);
+    };
+    auto stage_of = [&](int j) { return smem + ((j - kt0) % NS) * STAGE; };
+    f16x8 af[2][TM], bf[2][TN];
+    // one k16 sub-step: MFMAs on buffer bm, with the NF fragment reads of
+    // sub-step kkr of stage rd into buffer br interleaved
+    auto sub = [&](const f16* rd, int kkr, int br, int bm) {
 #pragma unroll
-      for (int i = 0; i < NS - 1; ++i)
-        if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
-    }
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int rel = kt - kt0;
-      f16* cur = smem + (rel % NS) * STAGE;
-      f16* nxt = smem + ((rel + NS - 1) % NS) * STAGE;  // the stage read in step kt - 1
-      if (copies) {
-        // wait for this wave's DMA of stage kt; the newer stages stay in flight
-        const int newer = min(NS - 2, kt1 - 1 - kt);
-        if (newer <= 0) PHI_WAIT_VMCNT(0);
-        else if (newer == 1) PHI_WAIT_VMCNT(LPW);
-        else PHI_WAIT_VMCNT(2 * LPW);
+      for (int f = 0; f < NF; ++f) ld1(rd, kkr, f, af[br], bf[br]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm][i], bf[bm][j], acc[i][j], 0, 0, 0);
+      // MFMAs first: a read ahead of them would make the first MFMA wait for
+      // it too (lgkmcnt(0)), a full LDS latency per sub-step
+#pragma unroll
+      for (int q = 0; q < NF; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      lds_barrier();
+      if (TM * TN > R * NF) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * NF, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (kt0 < kt1) {
       if (copies) {
-        if (kt + NS - 1 < kt1) issue(kt + NS - 1, nxt);
-        if (HW > 0) continue;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+          if (kt0 + i < kt1) issue(kt0 + i, smem + i * STAGE);
+        wait_stage(kt0);
       }
-      kstep(cur);
+      lds_barrier();  // B(kt0)
+      if (copies && kt0 + NS - 1 < kt1) issue(kt0 + NS - 1, stage_of(kt0 + NS - 1));
+      if (HW > 0 && copies) {
+        for (int j = kt0 + 1; j < kt1; ++j) {
+          wait_stage(j);
+          lds_barrier();  // B(j)
+          if (j + NS - 1 < kt1) issue(j + NS - 1, stage_of(j + NS - 1));
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) ld1(smem, 0, f, af[0], bf[0]);
+        for (int kt = kt0; kt < kt1; ++kt) {
+          const f16* cur = stage_of(kt);
+          sub(cur, 1, 1, 0);
+          sub(cur, 2, 0, 1);
+          sub(cur, 3, 1, 0);
+          const bool more = kt + 1 < kt1;
+          if (more) {
+            if (copies) wait_stage(kt + 1);
+            lds_barrier();  // B(kt + 1): this wave's reads of stage kt are done
+            if (copies && kt + NS < kt1) issue(kt + NS, stage_of(kt + NS));
+          }
+          // (the last k-step re-reads its own stage into the unused buffer: no
+          // branch around the MFMAs, which keeps the accumulators in place)
+          sub(more ? stage_of(kt + 1) : cur, 0, 0, 1);
+        }
+      }
     }
   }
 
