@@ -75,7 +75,7 @@ __device__ __forceinline__ void softmax_block(f32x16 (&sc)[NH], f32x16 (&o)[DB],
   for (int hb = 0; hb < NH; ++hb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[hb][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(mx);
   const float m_new = fmaxf(m_run, mx * c);  // finite: every lane has an unmasked key in its first block
   float psum = 0.f;
 #pragma unroll
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
   }
 
   // this wave's partial state -> LDS (query = col; d rows of O^T)
-  const float l_w = l_run + __shfl_xor(l_run, 32);
+  const float l_w = add_xor32(l_run);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -265,6 +265,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
   constexpr int NI = NK + NV, LPW = ((NK > NV ? NK : NV) + HW - 1) / HW;  // loads per wave and block
   constexpr int STG = NI * 1024;                          // bytes per stage
   constexpr int OLD = D + 8;                              // output staging row (f16)
+  constexpr bool kEarlyV = D <= 96;                       // value fragments read with the key fragments
   static_assert(NK * 64 == KB * KSLOT, "key slots fill whole instructions");
   static_assert(NWV * 32 * OLD * 2 <= NSTG * STG, "output staging fits");
   static_assert((8 / NWV) * NSTG * STG <= 160 * 1024, "workgroups per CU fit in LDS");
@@ -309,6 +310,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
       ldst[t] = (NK + jj) * 1024;
     }
   }
+  // The copies are buffer loads into LDS (MUBUF): the compiler counts a
+  // global (FLAT) load into LDS as an LDS access in flight as well, and then
+  // waits for lgkmcnt(0) before the first use of any later LDS read; with the
+  // buffer form each fragment read gets its own lgkmcnt wait.
+  const __amdgpu_buffer_rsrc_t krs = attn_rsrc(Kp, S * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = attn_rsrc(Vt, D * a.s_pad * 2);
   auto issue = [&](int blk, int stage) {
     const int key0 = blk * KB;
     char* st = lds + stage * STG;
@@ -316,13 +323,15 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
 #pragma unroll
       for (int t = 0; t < LPW; ++t) {
         // key rows past the sequence re-read the last row (their scores are masked)
-        const f16* gsrc = Kp + (size_t)min(key0 + lrow[t], S - 1) * D + loff[t];
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)gsrc, (lds_ptr_t)(st + ldst[t]), 16, 0, 0);
+        const int off = (min(key0 + lrow[t], S - 1) * D + loff[t]) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(st + ldst[t]), 16, off, 0, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < LPW; ++t)
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)(Vt + loff[t] + key0), (lds_ptr_t)(st + ldst[t]), 16, 0, 0);
+      for (int t = 0; t < LPW; ++t) {
+        const int off = (loff[t] + key0) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(st + ldst[t]), 16, off, 0, 0, 0);
+      }
     }
   };
 
@@ -354,18 +363,60 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
     if (j + PD < nb) issue(j + PD, (j + PD) % NSTG);
     const int key0 = j * KB;
     if (key0 > wave_last) continue;            // above this wave's diagonal (barriers still met)
-    const char* stg = lds + (j % NSTG) * STG;
-    const char* ks_base = stg;
-    const char* vs_base = stg + NK * 1024;
+    const char* ks_base = lds + (j % NSTG) * STG;
+    const char* vs_base = ks_base + NK * 1024;
+    // LDS fragment reads are issued in groups ahead of the MFMAs that use
+    // them, so a group pays the LDS latency once instead of once per MFMA.
+    // Up to head_dim 96 the whole block's key fragments go first, then the
+    // value fragments, which land under the score MFMAs and the softmax; at
+    // 128 (registers) the key fragments go per 32-key half and the value
+    // fragments per 16-key group, after the softmax.
+    auto read_v = [&](int hb, int hv, f16x8 (&v)[DB]) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + col, chunk = 4 * hb + 2 * hv + grp;
+        v[db] = *reinterpret_cast<const f16x8*>(vs_base + d * 128 + 16 * (chunk ^ ((d >> 1) & 7)));
+      }
+    };
+    f16x8 vf[kEarlyV ? 2 : 1][2][DB];
     f32x16 sc[2];
+    if constexpr (kEarlyV) {
+      f16x8 kf[2][KS];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      sc[hb] = f32x16{};
-      const char* krow = ks_base + (32 * hb + kr) * KSLOT * 16;
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(krow + (ks * 2 + grp) * 16);
-        sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sc[hb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks)
+          kf[hb][ks] = *reinterpret_cast<const f16x8*>(ks_base + ((32 * hb + kr) * KSLOT + ks * 2 + grp) * 16);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) read_v(hb, hv, vf[hb][hv]);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        sc[hb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hb][ks], qf[ks], sc[hb], 0, 0, 0);
+      }
+      // order: the key reads, then each score MFMA followed by one value
+      // read (2 KS MFMAs, 4 DB = 2 KS value reads)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f16x8 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[ks] = *reinterpret_cast<const f16x8*>(ks_base + ((32 * hb + kr) * KSLOT + ks * 2 + grp) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[hb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], sc[hb], 0, 0, 0);
       }
     }
     // keys past min(qi, S - 1) are masked, in blocks that reach the diagonal
@@ -376,25 +427,25 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int hv = 0; hv < 2; ++hv) {
+        f16x8 (&v)[DB] = vf[kEarlyV ? hb : 0][kEarlyV ? hv : 0];
+        if constexpr (!kEarlyV) read_v(hb, hv, v);
+        const int chunk = 4 * hb + 2 * hv + grp;
+        if (tail) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[db][e] = 8 * chunk + e < vlim ? v[db][e] : (f16)0.f;
+        }
         f16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[e] = (f16)sc[hb][8 * hv + e];
-        const int chunk = 4 * hb + 2 * hv + grp;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + col;
-          f16x8 vf = *reinterpret_cast<const f16x8*>(vs_base + d * 128 + 16 * (chunk ^ ((d >> 1) & 7)));
-          if (tail) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vf[e] = 8 * chunk + e < vlim ? vf[e] : (f16)0.f;
-          }
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
-        }
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v[db], pf, o[db], 0, 0, 0);
       }
   }
 
   // normalise, stage [query][d] through LDS, 16-byte stores
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = add_xor32(l_run);
   const float inv = wave_last >= q0 ? 1.0f / l_tot : 0.f;
   __syncthreads();  // every wave is done with the stages
   f16* so = reinterpret_cast<f16*>(lds) + w * 32 * OLD;

@@ -15,10 +15,15 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// Address spaces of the direct global -> LDS loads (global_load_lds_dwordx4:
-// each lane's 16 bytes land at the wave-uniform LDS address + 16 * lane).
+// LDS destination of the direct global -> LDS loads (buffer_load_dwordx4
+// with lds: each lane's 16 bytes land at the wave-uniform LDS address +
+// 16 * lane).  Every kernel issues them in the buffer (MUBUF) form: the
+// compiler treats the global (FLAT) form as an LDS access in flight as well,
+// which turns the per-read lgkmcnt waits of later LDS reads into
+// lgkmcnt(0).  An offset argument of the buffer builtin is passed as a named
+// variable: with an inline expression there, the host pass of this compiler
+// silently dropped the kernel's launch stub (an undefined symbol at load).
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 // Cache-policy operand of global loads: non-temporal (streamed data).
 constexpr int kCacheNT = 2;
@@ -43,6 +48,29 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
+}
+
+// Lane pairs (l, l ^ 32) and (l, l ^ 16) combined without an LDS round trip:
+// v_permlane32_swap / v_permlane16_swap of a value with itself leave, in the
+// two result registers of lane l, the values of lanes l and l ^ 32 (l ^ 16);
+// which register holds which depends on the half, so only symmetric
+// combinations are formed.  Both lanes of a pair get the same sum, operand
+// order included.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <class T> struct vec4;

@@ -97,20 +97,30 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(De
   }
 
   char* ring = lds + w * WB;
+  // Page copies are buffer loads into LDS over a resource per page (the
+  // page's (KV head) slab is wave-uniform; a pool may exceed the 32-bit
+  // offset range of one resource).  The buffer form, unlike a global load
+  // into LDS, leaves the compiler's per-read lgkmcnt waits on the fragment
+  // reads intact.
   auto issue = [&](int i) {
     const int phys = __builtin_amdgcn_readlane(my_phys, i);
     char* st = ring + (i % NST) * SB;
-    const char* kp = reinterpret_cast<const char*>(a.k_pool + ((size_t)phys * a.Hkv + g) * PG * D);
-    const char* vp = reinterpret_cast<const char*>(a.v_pool + ((size_t)phys * a.Hkv + g) * PG * D);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<f16*>(a.k_pool + ((size_t)phys * a.Hkv + g) * PG * D), 0, KBY, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.v_pool + ((size_t)phys * a.Hkv + g) * PG * D), 0, VBY, 0x00020000);
     const int r0 = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int j = 0; j < KBY / 1024; ++j) {  // token rows 4 j .. 4 j + 3; LDS slot c of row r takes chunk c ^ r
       const int r = 4 * j + r0;
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(kp + r * 256 + ((c ^ r) << 4)), (lds_ptr_t)(st + j * 1024), 16, 0, 0);
+      const int off = r * 256 + ((c ^ r) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(st + j * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < VBY / 1024; ++j)
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(vp + j * 1024 + lane * 16), (lds_ptr_t)(st + KBY + j * 1024), 16, 0, 0);
+    for (int j = 0; j < VBY / 1024; ++j) {
+      const int off = j * 1024 + lane * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(st + KBY + j * 1024), 16, off, 0, 0, 0);
+    }
   };
 
   for (int i = 0; i < NST - 1 && i < nw; ++i) issue(i);
@@ -163,8 +173,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(De
     }
     // 2. running max per head (lanes hl, hl + 16, hl + 32, hl + 48 share a head)
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_run, mx * c2);  // finite: the page's first token is valid
     float ps = 0.f;
 #pragma unroll
@@ -209,8 +218,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(De
     }
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = add_xor32(add_xor16(l_run));
   __syncthreads();  // every wave is done with its ring: reuse it for the merge
   float* s_o = reinterpret_cast<float*>(lds);            // [NWV][G][D]
   float* s_ml = s_o + NWV * G * D;                         // [NWV][G][2]

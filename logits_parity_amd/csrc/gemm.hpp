@@ -7,7 +7,7 @@
 //  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
 //    them in flight while one is consumed, so the DMA of a k-step has NS - 1
 //    k-steps of MFMA work to arrive.  Operands go global -> LDS directly
-//    (global_load_lds_dwordx4, no VGPR staging): one wave instruction fills
+//    (buffer_load_dwordx4 ... lds, no VGPR staging): one wave instruction fills
 //    1 KB = 8 binary16 rows of 128 B, or 16 int8 weight rows of 64 B.  int8
 //    codes are widened exactly to binary16 (|q| <= 127) as their fragments
 //    are read from LDS; the per-row scale multiplies the fp32 accumulator (it
@@ -230,8 +230,16 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 8;
     }
   }
+  // Buffer loads into LDS (MUBUF) rather than global ones (FLAT): the
+  // compiler counts a FLAT load into LDS as an LDS access in flight too, and
+  // then makes the first use of every later fragment read wait for
+  // lgkmcnt(0).  Byte offsets fit the 32-bit voffset: the host keeps each
+  // operand under 2^31 elements of at most 2 bytes.
   const f16* Wf = reinterpret_cast<const f16*>(a.W);
   const int8_t* W8p = reinterpret_cast<const int8_t*>(a.W);
+  constexpr int WBY = W8 ? 1 : 2;
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), 0, -1, 0x00020000);
 
   auto issue = [&](int kt, f16* st) {
     const int k0 = kt * BK;
@@ -241,9 +249,9 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       lds_ptr_t dst = (lds_ptr_t)(reinterpret_cast<char*>(st) + j * 1024);
       // weights are streamed once per tile row: non-temporal, so that they do
       // not push the activation tiles (re-read by every N-tile) out of L2
-      if (t < TA_) __builtin_amdgcn_global_load_lds((glb_ptr_t)(A + src_off[t] + k0), dst, 16, 0, 0);
-      else if constexpr (W8) __builtin_amdgcn_global_load_lds((glb_ptr_t)(W8p + src_off[t] + k0), dst, 16, 0, kCacheNT);
-      else __builtin_amdgcn_global_load_lds((glb_ptr_t)(Wf + src_off[t] + k0), dst, 16, 0, kCacheNT);
+      const unsigned off = (unsigned)(src_off[t] + k0) * (t < TA_ ? 2u : (unsigned)WBY);
+      if (t < TA_) __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 16, off, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, dst, 16, off, 0, 0, kCacheNT);
     }
   };
 
