@@ -244,8 +244,15 @@ __global__ __launch_bounds__(NKV * 64, 2) void phi_attn_prefill_f16_kernel(AttnA
 // [D][64] go global -> LDS by DMA into a ring of 3 stages (2 at head_dim
 // 128, where 3 would leave one workgroup per CU), the others ahead of the one
 // being read, and all four waves read them from LDS (one global read
-// per block per workgroup instead of one per wave).  Each wave keeps its own
-// online softmax over every block up to its diagonal, so no merge is needed.
+// per block per workgroup instead of one per wave).  With 8 waves a
+// workgroup owns 256 queries.  Each wave keeps its own online softmax over
+// every block up to its diagonal, so no merge is needed.  The softmax here
+// differs from the split-key kernel's in three ways that take VALU work off
+// the block loop: the queries are pre-scaled by log2(e) / sqrt(D); the score
+// MFMA starts from the lane's reference max (no per-score fma), and the
+// reference moves only when a block exceeds it by more than 8 (so P <= 2^8);
+// the row sums come from one more MFMA per 16 keys with an all-ones operand
+// instead of 32 adds.
 // LDS rows: a key row is D / 8 + 1 16-byte slots (the extra slot is padding
 // that makes the 32 rows of a fragment read conflict free); a V^T row is 8
 // slots with chunk' = chunk ^ ((d >> 1) & 7).  The MFMA formulation and the
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
   f32x16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m_run = -__builtin_inff(), l_run = 0.f;
+  float m_run = -__builtin_inff();  // the lane's reference b (log2 units of c s); -inf before its first block
 
   issue(0, 0);
   f16x8 qf[KS];
@@ -355,6 +362,24 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
   // first use inside the loop.
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  // queries pre-scaled by c = log2(e) / sqrt(D) (rounded to binary16), so
+  // the score MFMA yields c s directly, in log2 units
+  {
+    const float c = a.scale_log2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (f16)((float)qf[ks][e] * c);
+  }
+  // Lazy running max: the score MFMA accumulates onto -b (b: this lane's
+  // reference, negm its splat), so it yields c s - b; b moves only when a
+  // block's max exceeds it by more than kLazy (P then stays <= 2^kLazy) or
+  // on the lane's first block.  The row sums come from the value MFMA with
+  // an all-ones operand, i.e. from the same binary16 P as the output.
+  constexpr float kLazy = 8.f;
+  f32x16 negm = f32x16{};
+  f32x16 lacc = f32x16{};
+  const f16x8 ones = {(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
   for (int j = 0; j < nb; ++j) {
     // block j landed: only the (PD - 1) newer blocks' loads may still be in flight
     if (PD > 1 && j + 1 < nb) PHI_WAIT_VMCNT((PD - 1) * LPW);
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
         for (int hv = 0; hv < 2; ++hv) read_v(hb, hv, vf[hb][hv]);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        sc[hb] = f32x16{};
+        sc[hb] = negm;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[hb][ks], qf[ks], sc[hb], 0, 0, 0);
@@ -414,13 +439,46 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
         for (int ks = 0; ks < KS; ++ks)
           kf[ks] = *reinterpret_cast<const f16x8*>(ks_base + ((32 * hb + kr) * KSLOT + ks * 2 + grp) * 16);
         __builtin_amdgcn_sched_barrier(0);
-        sc[hb] = f32x16{};
+        sc[hb] = negm;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[ks], qf[ks], sc[hb], 0, 0, 0);
       }
     }
-    // keys past min(qi, S - 1) are masked, in blocks that reach the diagonal
-    softmax_block<2, DB>(sc, o, m_run, l_run, a.scale_log2, key0 + KB - 1 > q0, min(qi, S - 1) - key0 - 8 * grp);
+    if (key0 + KB - 1 > q0) {  // keys past min(qi, S - 1) are masked, in blocks that reach the diagonal
+      const int kmax = min(qi, S - 1) - key0 - 8 * grp;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[hb][v] = 32 * hb + 16 * (v >> 3) + (v & 7) > kmax ? -__builtin_inff() : sc[hb][v];
+    }
+    {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[hb][v]);
+      mx = max_xor32(mx);  // block max of c s - b (b = 0 before the lane's first block)
+      const bool first = m_run == -__builtin_inff();
+      const bool move = first || mx > kLazy;
+      if (__ballot(move)) {
+        const float delta = move ? mx : 0.f;  // finite: every lane has an unmasked key in its first block
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[hb][v] -= delta;
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        lacc *= alpha;
+        m_run = (first ? 0.f : m_run) + delta;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) negm[v] = -m_run;
+      }
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[hb][v] = __builtin_amdgcn_exp2f(sc[hb][v]);
     const bool tail = key0 + KB > S;  // value columns >= S are padding: zero them
     const int vlim = S - key0;
 #pragma unroll
@@ -441,11 +499,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_attn_prefill_lds_kernel
         for (int e = 0; e < 8; ++e) pf[e] = (f16)sc[hb][8 * hv + e];
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v[db], pf, o[db], 0, 0, 0);
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, pf, lacc, 0, 0, 0);
       }
   }
 
   // normalise, stage [query][d] through LDS, 16-byte stores
-  const float l_tot = add_xor32(l_run);
+  const float l_tot = lacc[0];  // every row of the ones product is the query's sum over all keys
   const float inv = wave_last >= q0 ? 1.0f / l_tot : 0.f;
   __syncthreads();  // every wave is done with the stages
   f16* so = reinterpret_cast<f16*>(lds) + w * 32 * OLD;

@@ -83,8 +83,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void phi_decode_stream_kernel(De
 #pragma unroll
     for (int k = 0; k < 4; ++k) qf[k] = *reinterpret_cast<const f16x8*>(qrow + 32 * k);
   }
-  // physical page of the wave's page i in lane i (lanes past nw re-read an entry in the row)
-  const int ti = min(p_begin + w + NWV * min(lane, max(nw - 1, 0)), a.max_pages - 1);
+  // physical page of the wave's page i in lane i; the row is read without
+  // waiting for the context length (lanes past nw read entries that are
+  // never used), so the length, table and query loads share one latency
+  const int ti = min(p_begin + w + NWV * lane, a.max_pages - 1);
   int my_phys = a.block_table[(size_t)b * a.max_pages + ti];
   if (lane < nw && (my_phys < 0 || my_phys >= a.n_pages)) err = true;
   if (__any(err)) {  // the split's result becomes NaN; read nothing
