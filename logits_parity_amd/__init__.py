@@ -113,7 +113,15 @@ def _check(status: int, where: str):
 
 
 def _ptr(t) -> int | None:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor the library reads or writes as a dense
+    row-major array: a strided view (a transpose, a broadcast, a slice with
+    steps) would be read in the wrong layout, so it is refused."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} and strides {tuple(t.stride())} is not contiguous; "
+                         "pass .contiguous()")
+    return t.data_ptr()
 
 
 def _stream(stream) -> int | None:
@@ -231,11 +239,11 @@ class KVCache:
 
     def struct(self, block_table=None) -> phi_kv_cache:
         bt = self.block_table if block_table is None else block_table
-        self._kp = (ctypes.c_void_p * len(self.k_pools))(*[t.data_ptr() for t in self.k_pools])
-        self._vp = (ctypes.c_void_p * len(self.v_pools))(*[t.data_ptr() for t in self.v_pools])
+        self._kp = (ctypes.c_void_p * len(self.k_pools))(*[_ptr(t) for t in self.k_pools])
+        self._vp = (ctypes.c_void_p * len(self.v_pools))(*[_ptr(t) for t in self.v_pools])
         return phi_kv_cache(ctypes.cast(self._kp, ctypes.POINTER(ctypes.c_void_p)),
-                            ctypes.cast(self._vp, ctypes.POINTER(ctypes.c_void_p)), self.v_scale.data_ptr(),
-                            bt.data_ptr(), self.k_pools[0].shape[0], bt.shape[1], 16)
+                            ctypes.cast(self._vp, ctypes.POINTER(ctypes.c_void_p)), _ptr(self.v_scale),
+                            _ptr(bt), self.k_pools[0].shape[0], bt.shape[1], 16)
 
     def with_table(self, block_table) -> "KVCache":
         """The same pools seen through another block table (e.g. one row)."""

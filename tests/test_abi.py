@@ -162,6 +162,24 @@ def test_noalloc_decode_rejects_before_any_hip_call():
     assert L.attn_decode_k16v8_workspace_bytes(3, 40, 10, 128, 3000) <= limit
 
 
+def test_binding_refuses_strided_tensors():
+    """The binding passes raw addresses, and the library reads every operand as
+    a dense row-major array: a strided view (a broadcast, a transpose, a
+    stepped slice) is refused in Python before any library call."""
+    import torch
+    base = torch.zeros((4, 6), dtype=torch.float16)
+    assert phi._ptr(None) is None
+    assert phi._ptr(base) == base.data_ptr()
+    assert phi._ptr(base[1:3]) == base[1:3].data_ptr()  # whole rows stay dense
+    for view in (base.t(), base[:, :3], base[::2], torch.zeros(6, dtype=torch.float16).expand(4, 6)):
+        with pytest.raises(ValueError, match="not contiguous"):
+            phi._ptr(view)
+    with pytest.raises(ValueError, match="not contiguous"):
+        phi.phi_attention_prefill(torch.zeros((1, 2, 8, 96), dtype=torch.float16).transpose(1, 2),
+                                  torch.zeros((1, 2, 8, 96), dtype=torch.float16),
+                                  torch.zeros((1, 2, 96, 64), dtype=torch.float16), out=base)
+
+
 def test_decode_plan_split_counts():
     # the decode workspace holds (o, max, sum) partials per (sequence, query
     # head, split), so its size shows the split plan: one split per sequence

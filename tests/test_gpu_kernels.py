@@ -162,6 +162,32 @@ def test_attention_f16_shared_key_blocks(phi, B, S, nh, nkv, D):
     assert np.all(np.abs(got - ref) <= 2e-3 + 2e-3 * np.abs(ref)), np.abs(got - ref).max()
 
 
+@pytest.mark.parametrize("direction", [1.0, -1.0], ids=["rising", "falling"])
+def test_attention_shared_key_blocks_moving_max(phi, direction):
+    """Scores that ramp along the keys by about 60 log2 units over the
+    sequence (rising: every query's maximum is its most recent key, so the
+    running maximum keeps moving by more than the kernel's lazy threshold;
+    falling: the first block holds the maximum and later blocks contribute
+    almost nothing), checked element by element against the oracle."""
+    B, S, nh, nkv, D = 1, 1537, 32, 32, 96
+    assert B * nh * (-(-S // 128)) >= 384
+    _say(f"attention f16 shared blocks, moving max ({'rising' if direction > 0 else 'falling'})")
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal((nh, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    ramp = direction * np.linspace(-1.0, 1.0, S)                  # g(t)
+    amp = 30.0 * np.sqrt(D) / np.log2(np.e)                        # c * a * g spans about +-30 log2 units
+    q = np.broadcast_to(u[None, :, None, :] * np.sqrt(amp), (B, nh, S, D))
+    k = u[None, :, None, :] * (np.sqrt(amp) * ramp)[None, None, :, None]
+    k = k + 0.05 * rng.standard_normal((B, nkv, S, D))
+    v = synth.normal(91, "attn.v", (B, nkv, S, D), 1.0, np.float16)
+    q, k = np.ascontiguousarray(q, dtype=np.float16), np.ascontiguousarray(k, dtype=np.float16)
+    got = _attn_gpu(phi, q, k, v)
+    ref = _attn_ref(q, k, v)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= 2e-3 + 2e-3 * np.abs(ref)), np.abs(got - ref).max()
+
+
 def test_attention_shared_key_blocks_rows_sum_to_one(phi):
     q, k, v = _attn_inputs(1, 3001, 16, 2, np.float16, 6, scale=2.0)
     got = _attn_gpu(phi, q, k, np.ones_like(v))
