@@ -140,6 +140,18 @@ size_t phi_workspace_bytes(const phi_model* m, int32_t batch, int32_t seq);
 phi_status phi_prefill_logits(const phi_model* m, const int32_t* ids, int32_t batch, int32_t seq,
                               float* logits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* phi_prefill_logits with the ids in host memory (the per-token logit dump
+ * of [P2] section 1 takes token ids from the caller's file).  Every id is
+ * checked on the host first: one outside [0, V) returns PHI_E_RANGE, as do
+ * the checks of phi_prefill_logits, before anything is enqueued.  The ids are
+ * then copied on `stream` into a region of the same workspace
+ * (phi_workspace_bytes covers it), so ids_host must stay valid and unchanged
+ * until the stream has run that copy, as for any asynchronous host-to-device
+ * copy (from pageable memory HIP has read it before returning).  The result
+ * is identical to phi_prefill_logits on the same ids. */
+phi_status phi_prefill_logits_host_ids(const phi_model* m, const int32_t* ids_host, int32_t batch, int32_t seq,
+                                       float* logits, void* workspace, size_t workspace_bytes, void* stream);
+
 void phi_free(phi_model* m);
 
 /* Static text for a status code. */

@@ -25,7 +25,7 @@ EXPORTS = ("phi_state_bytes", "phi_load_fused", "phi_workspace_bytes", "phi_pref
            "phi_strerror", "phi_linear_f32out", "phi_gate_up_silu", "phi_attention_vt_stride", "phi_attention_prefill",
            "attn_decode_k16v8_workspace_bytes", "attn_decode_k16v8", "phi_kv_pool_slots", "phi_profile_enable",
            "phi_profile_read", "kv_append_k16v8", "phi_prefill_fill_k16v8", "phi_decode_workspace_bytes",
-           "phi_decode_step_k16v8", "attn_decode_k16v8_noalloc")
+           "phi_decode_step_k16v8", "attn_decode_k16v8_noalloc", "phi_prefill_logits_host_ids")
 
 
 class PhiError(RuntimeError):
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(P)]),
         "phi_workspace_bytes": (sz, [P, i32, i32]),
         "phi_prefill_logits": (i32, [P, P, i32, i32, P, P, sz, P]),
+        "phi_prefill_logits_host_ids": (i32, [P, P, i32, i32, P, P, sz, P]),
         "phi_free": (None, [P]),
         "phi_strerror": (ctypes.c_char_p, [i32]),
         "phi_linear_f32out": (i32, [i32, P, P, P, P, i32, i32, i32, P]),
@@ -268,6 +269,32 @@ def phi_prefill_logits(model: Model, ids, logits=None, workspace=None, stream=No
     _check(lib().phi_prefill_logits(model.handle, _ptr(ids), B, S, _ptr(logits), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "phi_prefill_logits")
+    return logits
+
+
+def phi_prefill_logits_host_ids(model: Model, ids, logits, workspace=None, stream=None):
+    """ids: int32 host array or CPU tensor [B, S], checked against the
+    vocabulary by the library before anything is enqueued -> float32 logits
+    [B, S, V] on the device of `logits`.  The ids buffer must stay unchanged
+    until the stream has run the copy."""
+    import numpy as np
+    import torch
+    if isinstance(ids, np.ndarray):
+        if ids.dtype != np.int32 or not ids.flags["C_CONTIGUOUS"]:
+            raise ValueError("ids must be a C-contiguous int32 array")
+        B, S = ids.shape
+        ids_addr = ids.ctypes.data
+    else:
+        if ids.dtype != torch.int32 or ids.device.type != "cpu":
+            raise ValueError("ids must be an int32 CPU tensor")
+        B, S = ids.shape
+        ids_addr = _ptr(ids)
+    need = model.workspace_bytes(B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    _check(lib().phi_prefill_logits_host_ids(model.handle, ids_addr, B, S, _ptr(logits), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)),
+           "phi_prefill_logits_host_ids")
     return logits
 
 

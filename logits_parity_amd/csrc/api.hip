@@ -200,7 +200,7 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
 struct PrefillPlan {
   int T, S, s_pad;
   GemmPlan qkv, o, gu, down, lm;
-  size_t off_x, off_xn, off_q, off_k, off_vt, off_attn, off_act, off_part, total;
+  size_t off_x, off_xn, off_q, off_k, off_vt, off_attn, off_act, off_part, off_ids, total;
 };
 
 PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
@@ -228,6 +228,7 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.off_act = take(T * (size_t)I * as);
   const int max_split = c.wtype == PHI_WT_F32 ? 0 : std::max(p.o.splits, p.down.splits);
   p.off_part = take(max_split > 1 ? (size_t)max_split * T * H * 4 : 0);
+  p.off_ids = take(T * 4);  // the device copy of host ids (phi_prefill_logits_host_ids)
   p.total = o;
   return p;
 }
@@ -962,6 +963,26 @@ phi_status phi_prefill_logits(const phi_model* m, const int32_t* ids, int32_t ba
   if (pr.enabled && pr.used + launches_per_forward(m->cfg) > pr.stage.size()) return PHI_E_RANGE;
   if (m->cfg.wtype == PHI_WT_F32) return forward<float>(m, ids, batch, seq, logits, ws, st);
   return forward<f16>(m, ids, batch, seq, logits, ws, st);
+}
+
+phi_status phi_prefill_logits_host_ids(const phi_model* m, const int32_t* ids_host, int32_t batch, int32_t seq,
+                                       float* logits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!m || !ids_host || !logits || !workspace) return PHI_E_NULL;
+  if (batch < 1 || seq < 1) return PHI_E_SHAPE;
+  if (seq > m->cfg.max_pos) return PHI_E_RANGE;
+  if (!rows_fit(m->cfg, (long long)batch * seq)) return PHI_E_SHAPE;
+  const PrefillPlan p = plan_prefill(m->cfg, batch, seq);
+  if (workspace_bytes < p.total) return PHI_E_WORKSPACE;
+  if (!aligned16(logits) || !aligned16(workspace)) return PHI_E_ALIGN;
+  const size_t T = (size_t)batch * seq;
+  for (size_t t = 0; t < T; ++t)
+    if (ids_host[t] < 0 || ids_host[t] >= m->cfg.vocab) return PHI_E_RANGE;
+  const PhiProfile& pr = m->prof;
+  if (pr.enabled && pr.used + launches_per_forward(m->cfg) > pr.stage.size()) return PHI_E_RANGE;
+  int32_t* ids_dev = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + p.off_ids);
+  if (hipMemcpyAsync(ids_dev, ids_host, T * sizeof(int32_t), hipMemcpyHostToDevice, as_stream(stream)) != hipSuccess)
+    return PHI_E_HIP;
+  return phi_prefill_logits(m, ids_dev, batch, seq, logits, workspace, workspace_bytes, stream);
 }
 
 void phi_free(phi_model* m) {

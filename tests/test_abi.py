@@ -162,6 +162,15 @@ def test_noalloc_decode_rejects_before_any_hip_call():
     assert L.attn_decode_k16v8_workspace_bytes(3, 40, 10, 128, 3000) <= limit
 
 
+def test_host_ids_entry_point_rejects_null_arguments():
+    """phi_prefill_logits_host_ids checks its pointers before anything else."""
+    L = phi.lib()
+    ids = (ctypes.c_int32 * 4)(0, 1, 2, 3)
+    assert L.phi_prefill_logits_host_ids(None, ids, 1, 4, 0x1000, 0x2000, 1 << 20, None) == 1
+    assert L.phi_prefill_logits_host_ids(0x100, None, 1, 4, 0x1000, 0x2000, 1 << 20, None) == 1
+    assert L.phi_prefill_logits_host_ids(0x100, ids, 1, 4, None, 0x2000, 1 << 20, None) == 1
+
+
 def test_binding_refuses_strided_tensors():
     """The binding passes raw addresses, and the library reads every operand as
     a dense row-major array: a strided view (a broadcast, a transpose, a

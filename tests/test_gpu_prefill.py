@@ -135,6 +135,37 @@ def test_tiny_errors_are_reported(phi):
     assert e.value.status == 5  # PHI_E_WORKSPACE
 
 
+@pytest.mark.parametrize("wtype", ["f32", "f16"])
+def test_tiny_host_ids_entry_point(phi, wtype):
+    """phi_prefill_logits_host_ids: the same logits, bit for bit, as the
+    device-ids entry point; an id outside [0, V) is refused on the host with
+    PHI_E_RANGE and nothing is enqueued (the logits buffer keeps its
+    sentinel)."""
+    from logits_parity_amd.weights import to_device
+    cfg = synth.TINY if wtype == "f32" else replace(synth.TINY, wtype=wtype)
+    ws = synth.WeightSet(cfg)
+    m = phi.phi_load_fused(cfg, to_device(ws, cfg.n_layers))
+    ids = np.ascontiguousarray(synth.token_ids(cfg, 2, 11), dtype=np.int32)
+    want = m.prefill_logits(torch.from_numpy(ids).cuda())
+    got = torch.empty_like(want)
+    phi.phi_prefill_logits_host_ids(m, ids, got)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    got_t = torch.full_like(want, 7.0)
+    phi.phi_prefill_logits_host_ids(m, torch.from_numpy(ids), got_t)
+    torch.cuda.synchronize()
+    assert torch.equal(got_t, want)
+    for bad in (-1, cfg.vocab):
+        ids_bad = ids.copy()
+        ids_bad[1, 4] = bad
+        sentinel = torch.full_like(want, 7.0)
+        with pytest.raises(phi.PhiError) as e:
+            phi.phi_prefill_logits_host_ids(m, ids_bad, sentinel)
+        assert e.value.status == 4  # PHI_E_RANGE
+        torch.cuda.synchronize()
+        assert bool((sentinel == 7.0).all())
+
+
 def test_mini_one_layer_ragged_1100_vs_oracle(phi):
     """Full Phi-3-mini width, one layer, 1100 tokens: the 1024-token-and-up
     GEMM tiles (QKV 256 x 192, gate/up and lm_head 256 x 256) with a ragged
