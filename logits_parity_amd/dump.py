@@ -49,10 +49,16 @@ def dump(model_dir: str, ids: np.ndarray, wtype: str = "f16", device: str = "cud
     if cfg.sliding_window is not None and S > cfg.sliding_window:
         raise ValueError(f"sequence length {S} exceeds the checkpoint's sliding window {cfg.sliding_window}, "
                          "which this engine does not apply")
-    if ids.min() < 0 or ids.max() >= cfg.vocab:
-        raise ValueError(f"ids must lie in [0, {cfg.vocab})")
     model = phi.phi_load_fused(cfg, weights)
-    logits = model.prefill_logits(torch.from_numpy(np.ascontiguousarray(ids)).to(device))
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    logits = torch.empty((B, S, cfg.vocab), dtype=torch.float32, device=device)
+    try:
+        # host ids: the library range-checks them before anything is enqueued
+        phi.phi_prefill_logits_host_ids(model, ids, logits)
+    except phi.PhiError as e:
+        if e.status == 4:  # PHI_E_RANGE
+            raise ValueError(f"ids must lie in [0, {cfg.vocab})") from e
+        raise
     torch.cuda.synchronize()
     return logits.cpu().numpy()
 
