@@ -2,8 +2,13 @@
 //
 // MFMA core (binary16 activations; binary16 or int8 weights):
 //  - 4 or 8 compute waves of 64 lanes, each owning a WM x WN sub-tile built
-//    from v_mfma_f32_32x32x16_f16 blocks with fp32 accumulators, plus
-//    optional copy waves that only issue the global -> LDS copies.
+//    from v_mfma_f32_16x16x32_f16 blocks with fp32 accumulators, plus
+//    optional copy waves that only issue the global -> LDS copies.  The
+//    16x16x32 form does the same flops per cycle as 32x32x16 but moves half
+//    the accumulator bytes per flop; under sustained load the chip's clock is
+//    set by its power limit, and with it the GEMMs ran at a higher shader
+//    clock (1.52 -> 1.75 GHz at 512 tokens, 1.78 -> 2.0 GHz at 4096, read from
+//    the shader-cycle and 100 MHz counters inside the kernel) and faster.
 //  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
 //    them in flight while one is consumed, so the DMA of a k-step has NS - 1
 //    k-steps of MFMA work to arrive.  Operands go global -> LDS directly
@@ -17,36 +22,35 @@
 //    at one logical chunk touch 16 distinct 16-byte bank groups of the
 //    256-byte LDS bank row, so fragment reads are conflict free (int8 rows:
 //    chunk' = chunk ^ ((row >> 1) & 3) over their four chunks).
-//  - Fragments are double-buffered over the four k16 sub-steps of a k-step:
-//    the reads for sub-step s + 1 are interleaved behind the MFMAs of
-//    sub-step s (scheduling barriers keep the compiler from re-serialising
-//    them).  The stage barrier of k-step kt + 1 sits before the last
-//    sub-step of kt, so the next stage's first reads also run under MFMAs.
+//  - A k-step is two k32 sub-steps.  The reads for sub-step s + 1 run behind
+//    the MFMAs of sub-step s: the operand with more blocks per wave is
+//    streamed (block o of the next sub-step is read into the registers of
+//    block o right after its last MFMA), the other one is double-buffered,
+//    and scheduling barriers keep the compiler from re-serialising them.  The
+//    stage barrier of k-step kt + 1 sits between the two sub-steps of kt, so
+//    the next stage's first reads also run under MFMAs.
 //  - Split-K: a launch may cut K into `splits` ranges; each writes an fp32
 //    partial tile that the next kernel (the residual + RMSNorm) reduces in a
 //    fixed order, so results do not depend on scheduling.
 //  - Workgroups map to tiles so that consecutive tiles of one weight column
 //    block run on the same XCD (workgroups go round-robin over the 8 XCDs),
 //    sharing that XCD's L2 for the weight tile.
-// Epilogues work on the accumulator registers (lane l of a 32x32 block holds
-// column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4, v < 16):
+// Epilogues work on the accumulator registers (lane l of a 16x16 block holds
+// column l % 16 and rows 4 (l / 16) + v, v < 4):
 //  EPI_F32      logits: out[m][n] = acc
 //  EPI_RESID    residual: x[m][n] += acc
 //  EPI_PARTIAL  split-K: part[split][m][n] = acc
-//  EPI_SILU     fused gate/up: the tile reads weight rows in 32-row blocks
+//  EPI_SILU     fused gate/up: the tile reads weight rows in 16-row blocks
 //               alternating gate, up for the same outputs, so a lane holds
 //               gate and up of one output: act = silu(gate) * up
 //  EPI_QKV      fused Q/K/V, one head (64, 96 or 128 wide) per wave, plus an
-//               optional per-row bias before RoPE: the head's
-//               weight rows are read in an order that puts RoPE pairs
-//               (d, d + HD / 2) in one lane (HD = 128: blocks 0..31 | 64..95 |
-//               32..63 | 96..127) or, for the third block of HD = 96 (rows
-//               0..31 | 48..79 | 32..47, 80..95), in lanes l and l ^ 16.  The
-//               RoPE position is the row's index within its sequence, or a
-//               per-row position (decode steps).  RoPE runs on the fp32
-//               accumulator; the head tile is staged through LDS in natural
-//               d order and written with 16-byte stores: Q, K to
-//               [B][heads][S][96], V to V^T [B][kv_heads][96][s_pad].
+//               optional per-row bias before RoPE.  With 16-wide blocks in
+//               natural d order, RoPE partners (d, d + HD / 2) sit in blocks
+//               j and j + HD / 32 of the same lane.  The RoPE position is the
+//               row's index within its sequence, or a per-row position
+//               (decode steps).  RoPE runs on the fp32 accumulator; the head
+//               tile is staged through LDS and written with 16-byte stores:
+//               Q, K to [B][heads][S][HD], V to V^T [B][kv_heads][HD][s_pad].
 // fp32 core (float32 model): a SIMT kernel with an LDS-staged epilogue.
 #pragma once
 #include <type_traits>
@@ -82,31 +86,14 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- row maps
-// Position of fused row j (< HD) inside its head for the QKV tiles: RoPE
-// partners (d, d + HD / 2) land in one lane of two 32-row blocks.
-//   HD = 96:  blocks hold d = 0..31 | 48..79 | 32..47, 80..95 (the third
-//             block's partners sit in lanes l and l ^ 16)
-//   HD = 128: blocks hold d = 0..31 | 64..95 | 32..63 | 96..127
-//   HD = 64:  blocks hold d = 0..31 | 32..63 (natural order)
-template <int HD>
-__device__ __forceinline__ int qkv_head_row(int j) {
-  if constexpr (HD == 64) return j;  // blocks 0..31 | 32..63 already pair up
-  else if constexpr (HD == 96) return j < 32 ? j : (j < 64 ? j + 16 : (j < 80 ? j - 32 : j));
-  else return j < 32 ? j : (j < 64 ? j + 32 : (j < 96 ? j - 32 : j));
-}
-
-// Weight row read by tile-local row r of N-tile tn (MFMA core).  HD: the QKV
-// head width (the wave tile width of QKV tiles).
-template <int EPI, int BN, int HD = 96>
+// Weight row read by tile-local row r of N-tile tn (MFMA core).
+template <int EPI, int BN>
 __device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
   if constexpr (EPI == EPI_SILU) {
-    // 32-row blocks alternate gate / up; block pair p covers outputs tn*BN/2 + 32p ..
-    const int blk = r >> 5, p = blk >> 1;
-    const int out = tn * (BN / 2) + p * 32 + (r & 31);
+    // 16-row blocks alternate gate / up; block pair p covers outputs tn*BN/2 + 16p ..
+    const int blk = r >> 4, p = blk >> 1;
+    const int out = tn * (BN / 2) + p * 16 + (r & 15);
     return (blk & 1) ? (a.N >> 1) + out : out;
-  } else if constexpr (EPI == EPI_QKV) {
-    const int n = tn * BN + (r / HD) * HD + qkv_head_row<HD>(r % HD);
-    return n < a.N ? n : a.N - 1;
   } else {
     const int n = tn * BN + r;
     return n < a.N ? n : a.N - 1;
@@ -140,7 +127,7 @@ template <int BM_, int BN_, int WGM_, int WGN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static constexpr int NT = WGM * WGN * 64, NW = WGM * WGN;
-  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 16, TN = WN / 16;  // 16x16 blocks per wave
 };
 
 // HW > 0 adds HW copy waves to the workgroup: they issue every global -> LDS
@@ -173,7 +160,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   constexpr bool PAD = LPW * NDW != INS_A + INS_W;
   constexpr int JMAX = INS_A + INS_W - 1;             // last copy of a stage
   static_assert(LPW * NDW == INS_A + INS_W || VG, "stage split (binary16 DMA tiles divide evenly)");
-  static_assert(TM * 32 == WM && TN * 32 == WN, "wave tile");
+  static_assert(TM * 16 == WM && TN * 16 == WN, "wave tile");
   static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
   constexpr int HD = EPI == EPI_QKV ? WN : 96;
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
@@ -224,10 +211,10 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       src_off[t] = (m0 + r < a.M ? m0 + r : a.M - 1) * K + c * 8;
     } else if constexpr (W8) {
       const int sw = s - INS_A * 64, r = sw >> 2, c = (sw & 3) ^ ((r >> 1) & 3);
-      src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 16;
+      src_off[t] = w_row_mfma<EPI, BN>(a, tn, r) * K + c * 16;
     } else {
       const int sw = s - INS_A * 64, r = sw >> 3, c = (sw & 7) ^ ((r >> 1) & 7);
-      src_off[t] = w_row_mfma<EPI, BN, HD>(a, tn, r) * K + c * 8;
+      src_off[t] = w_row_mfma<EPI, BN>(a, tn, r) * K + c * 8;
     }
   }
   // Buffer loads into LDS (MUBUF) rather than global ones (FLAT): the
@@ -255,63 +242,83 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     }
   };
 
-  f32x16 acc[TM][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{};
 
-  // fragment f of sub-step kk (16 of the stage's 64 k): f < TN is the B
-  // fragment of column block f, then the A fragments of row blocks f - TN
-  auto ld1 = [&](const f16* cur, int kk, int f, f16x8* fa, f16x8* fb) {
-    const int c = kk * 2 + (lane >> 5);
-    if (f < TN) {
-      const int r = wn * WN + f * 32 + (lane & 31);
-      if constexpr (W8) {
-        const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
-        const uint2 q = *reinterpret_cast<const uint2*>(curw + r * 64 + 16 * (kk ^ ((r >> 1) & 3)) + 8 * (lane >> 5));
-        fb[f] = i8x8_to_f16x8(q.x, q.y);
-      } else {
-        fb[f] = *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, c));
-      }
+  // Fragments of k32 sub-step kk (k = 32 kk .. 32 kk + 31 of the stage): A
+  // block i is 16 rows x 32 k, B block j 16 columns x 32 k; lane l holds row
+  // (column) l % 16 and k = 32 kk + 8 (l / 16) .. + 8.
+  auto ldA = [&](const f16* cur, int kk, int i) __attribute__((always_inline)) -> f16x8 {
+    const int r = wm * WM + i * 16 + (lane & 15);
+    return *reinterpret_cast<const f16x8*>(cur + swz(r, kk * 4 + (lane >> 4)));
+  };
+  auto ldB = [&](const f16* cur, int kk, int j) __attribute__((always_inline)) -> f16x8 {
+    const int r = wn * WN + j * 16 + (lane & 15);
+    if constexpr (W8) {
+      // the lane's 8 codes: 16-code chunk 2 kk + g / 2, half g % 2 (g = l / 16)
+      const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
+      const int g = lane >> 4;
+      const uint2 q = *reinterpret_cast<const uint2*>(curw + r * 64 + 16 * ((kk * 2 + (g >> 1)) ^ ((r >> 1) & 3)) +
+                                                      8 * (g & 1));
+      return i8x8_to_f16x8(q.x, q.y);
     } else {
-      fa[f - TN] = *reinterpret_cast<const f16x8*>(cur + swz(wm * WM + (f - TN) * 32 + (lane & 31), c));
+      return *reinterpret_cast<const f16x8*>(cur + BM * BK + swz(r, kk * 4 + (lane >> 4)));
     }
   };
-  // One k-step on stage `cur`: the next sub-step's fragment reads are
-  // interleaved one per R MFMAs with this sub-step's MFMAs.
-  auto kstep = [&](const f16* cur) {
-    constexpr int NF = TM + TN;
-    f16x8 af[2][TM], bf[2][TN];
+  // The operand with more blocks per wave is streamed in place (so[o]), the
+  // other one double-buffered (di[b][n]).  ROWS: A streams (TM >= TN).
+  constexpr bool ROWS = TM >= TN;
+  constexpr int NO = ROWS ? TM : TN, NI = ROWS ? TN : TM;
+  f16x8 so[NO], di[2][NI];
+  auto ld_o = [&](const f16* cur, int kk, int o) __attribute__((always_inline)) { return ROWS ? ldA(cur, kk, o) : ldB(cur, kk, o); };
+  auto ld_i = [&](const f16* cur, int kk, int n) __attribute__((always_inline)) { return ROWS ? ldB(cur, kk, n) : ldA(cur, kk, n); };
+  // One k32 sub-step: the MFMAs on so[] and di[b], outer block by outer
+  // block; with reads, the fragments of sub-step kkr of stage rd follow each
+  // outer block's MFMAs (its own streamed block, and the inner blocks spread
+  // evenly over the outer ones, into di[b ^ 1]).  MFMAs go first: a read ahead of them would make
+  // the first MFMA wait for it too (lgkmcnt(0)), a full LDS latency.
+  auto sub = [&](const f16* rd, int kkr, int b, auto reads) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) ld1(cur, 0, f, af[0], bf[0]);
+    for (int o = 0; o < NO; ++o) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) ld1(cur, kk + 1, f, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+      for (int n = 0; n < NI; ++n) {
+        if constexpr (ROWS) acc[o][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(so[o], di[b][n], acc[o][n], 0, 0, 0);
+        else acc[n][o] = __builtin_amdgcn_mfma_f32_16x16x32_f16(di[b][n], so[o], acc[n][o], 0, 0, 0);
       }
+      if constexpr (decltype(reads)::value) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk & 1][i], bf[kk & 1][j], acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      constexpr int R = (TM * TN) / NF > 0 ? (TM * TN) / NF : 1;
-      if (kk + 1 < 4) {
-#pragma unroll
-        for (int q = 0; q < NF; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
-        }
-        if (TM * TN > R * NF) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * NF, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        for (int n = o * NI / NO; n < (o + 1) * NI / NO; ++n) di[b ^ 1][n] = ld_i(rd, kkr, n);
+        so[o] = ld_o(rd, kkr, o);
       }
     }
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
+      if constexpr (decltype(reads)::value) {
+        const int nr = 1 + (o + 1) * NI / NO - o * NI / NO;  // reads after this outer block
+        if (nr == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        else if (nr == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (nr == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // sub-step 0 of a stage into so[] and di[0]
+  auto ld_first = [&](const f16* cur) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < NI; ++n) di[0][n] = ld_i(cur, 0, n);  // (row 0 needs all of these first)
+#pragma unroll
+    for (int o = 0; o < NO; ++o) so[o] = ld_o(cur, 0, o);
+  };
+  // One k-step on stage `cur` (register-staged path)
+  auto kstep = [&](const f16* cur) __attribute__((always_inline)) {
+    ld_first(cur);
+    sub(cur, 1, 0, std::true_type{});
+    sub(cur, 0, 1, std::false_type{});
   };
 
   const int kt0 = split * a.kt_per_split;
@@ -363,14 +370,12 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       lds_barrier();
     }
   } else {
-    // The stage barrier of k-step kt + 1 sits before the last k16 sub-step
-    // of k-step kt: every fragment of stage kt is in registers by then, so
-    // the next stage's first fragment reads run under kt's last MFMAs instead
-    // of in front of the next k-step's first ones.  Barrier B(j) (stage j has
-    // landed, every read of stage j - 2 is done) lets the copying waves fill
-    // stage (j - 1) % NS with k-step j + NS - 1.
-    constexpr int NF = TM + TN;
-    constexpr int R = (TM * TN) / NF > 0 ? (TM * TN) / NF : 1;
+    // The stage barrier of k-step kt + 1 sits between the two sub-steps of
+    // k-step kt: every fragment of stage kt is in registers by then, so the
+    // next stage's first fragment reads run under kt's second sub-step
+    // instead of in front of the next k-step's first MFMAs.  Barrier B(j)
+    // (stage j has landed, every read of stage j - 1 is done) lets the
+    // copying waves refill the stage of k-step j - 1 with k-step j + NS - 1.
     auto wait_stage = [&](int j) {  // this wave's DMA of stage j; newer stages stay in flight
       const int newer = min(NS - 2, kt1 - 1 - j);
       if (newer <= 0) PHI_WAIT_VMCNT(0);
@@ -378,27 +383,6 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
       else PHI_WAIT_VMCNT(2 * LPW);
     };
     auto stage_of = [&](int j) { return smem + ((j - kt0) % NS) * STAGE; };
-    f16x8 af[2][TM], bf[2][TN];
-    // one k16 sub-step: MFMAs on buffer bm, with the NF fragment reads of
-    // sub-step kkr of stage rd into buffer br interleaved
-    auto sub = [&](const f16* rd, int kkr, int br, int bm) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) ld1(rd, kkr, f, af[br], bf[br]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm][i], bf[bm][j], acc[i][j], 0, 0, 0);
-      // MFMAs first: a read ahead of them would make the first MFMA wait for
-      // it too (lgkmcnt(0)), a full LDS latency per sub-step
-#pragma unroll
-      for (int q = 0; q < NF; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (TM * TN > R * NF) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - R * NF, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
     if (kt0 < kt1) {
       if (copies) {
 #pragma unroll
@@ -415,22 +399,19 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
           if (j + NS - 1 < kt1) issue(j + NS - 1, stage_of(j + NS - 1));
         }
       } else {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) ld1(smem, 0, f, af[0], bf[0]);
+        ld_first(smem);
         for (int kt = kt0; kt < kt1; ++kt) {
           const f16* cur = stage_of(kt);
-          sub(cur, 1, 1, 0);
-          sub(cur, 2, 0, 1);
-          sub(cur, 3, 1, 0);
+          sub(cur, 1, 0, std::true_type{});
           const bool more = kt + 1 < kt1;
           if (more) {
             if (copies) wait_stage(kt + 1);
             lds_barrier();  // B(kt + 1): this wave's reads of stage kt are done
             if (copies && kt + NS < kt1) issue(kt + NS, stage_of(kt + NS));
           }
-          // (the last k-step re-reads its own stage into the unused buffer: no
+          // (the last k-step re-reads its own stage into the unused buffers: no
           // branch around the MFMAs, which keeps the accumulators in place)
-          sub(more ? stage_of(kt + 1) : cur, 0, 0, 1);
+          sub(more ? stage_of(kt + 1) : cur, 0, 1, std::true_type{});
         }
       }
     }
@@ -441,24 +422,24 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     if constexpr (EPI == EPI_QKV) __syncthreads();  // the one barrier of the QKV epilogue
     return;
   }
-  const int grp = lane >> 5, col_l = lane & 31;
-  auto row_of = [&](int i, int v) { return m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3); };
+  const int grp = lane >> 4, col_l = lane & 15;
+  auto row_of = [&](int i, int v) { return m0 + wm * WM + i * 16 + 4 * grp + v; };
   float sc[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     sc[j] = 1.0f;
-    if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN, HD>(a, tn, wn * WN + j * 32 + col_l)];
+    if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN>(a, tn, wn * WN + j * 16 + col_l)];
   }
 
   if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_PARTIAL) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = tn * BN + wn * WN + j * 32 + col_l;
+      const int n = tn * BN + wn * WN + j * 16 + col_l;
       if (n >= a.N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 4; ++v) {
           const int m = row_of(i, v);
           if (m >= a.M) continue;
           const float y = acc[i][j][v] * sc[j];
@@ -471,11 +452,11 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     f16* act = reinterpret_cast<f16*>(a.act);
 #pragma unroll
     for (int p = 0; p < TN / 2; ++p) {
-      const int n = tn * (BN / 2) + wn * (WN / 2) + p * 32 + col_l;
+      const int n = tn * (BN / 2) + wn * (WN / 2) + p * 16 + col_l;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 4; ++v) {
           const int m = row_of(i, v);
           if (m >= a.M) continue;
           act[(size_t)m * a.ld_act + n] = (f16)silu_mul(acc[i][2 * p][v] * sc[2 * p], acc[i][2 * p + 1][v] * sc[2 * p + 1]);
@@ -495,24 +476,20 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     const bool is_v = col0 >= k_end;
     const int head = col0 < q_end ? col0 / HD : (col0 < k_end ? (col0 - q_end) / HD : (col0 - k_end) / HD);
     const int nheads = col0 < q_end ? a.nh : a.nkv;
-    // natural d of each accumulator block for this lane, and the frequency of
-    // the pair the block belongs to (blocks 0, 1 and, for HD = 128, 2, 3 pair up)
-    int dd[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) dd[j] = qkv_head_row<HD>(j * 32 + col_l);
-    const int fA = col_l;                                            // blocks 0, 1
-    const int fB = HD == 96 ? 32 + (col_l & 15) : (HD == 128 ? 32 + col_l : 0);  // block 2 (and 3)
+    // block j < NP holds d = 16 j + l % 16 (frequency index f = d), block
+    // j + NP its RoPE partner d + HD / 2
+    constexpr int NP = HD / 32;
     const int mw0 = m0 + wm * WM;      // first token row of this wave
     // rotation factors of the lane's rows: all loads in flight at once, before
     // the barrier.  Position = pos[row] when given, else row mod S.
-    float cA[TM][16], sA[TM][16], cB[TM][16], sB[TM][16];
+    float cs[TM][4][NP], sn[TM][4][NP];
     if (!is_v && col0 < a.N) {
       const int s_base = mw0 - (mw0 / a.S) * a.S;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * grp + v;
           int sp;
           if (a.pos) {
             sp = a.pos[min(mw0 + r, a.M - 1)];
@@ -522,11 +499,10 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
             while (sp >= a.S) sp -= a.S;
           }
           const size_t t = (size_t)sp * HALF;
-          cA[i][v] = a.rope_cos[t + fA];
-          sA[i][v] = a.rope_sin[t + fA];
-          if constexpr (HD > 64) {
-            cB[i][v] = a.rope_cos[t + fB];
-            sB[i][v] = a.rope_sin[t + fB];
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            cs[i][v][q] = a.rope_cos[t + q * 16 + col_l];
+            sn[i][v][q] = a.rope_sin[t + q * 16 + col_l];
           }
         }
     }
@@ -534,7 +510,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     float bj[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bj[j] = (a.bias && col0 < a.N) ? (float)a.bias[w_row_mfma<EPI, BN, HD>(a, tn, wn * WN + j * 32 + col_l)] : 0.f;
+      bj[j] = (a.bias && col0 < a.N) ? (float)a.bias[w_row_mfma<EPI, BN>(a, tn, wn * WN + j * 16 + col_l)] : 0.f;
     __syncthreads();                      // every wave is done with the k-stages
     if (col0 >= a.N) return;
     f16* tile = smem + wave * REG;
@@ -542,28 +518,23 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * grp + v;
 #pragma unroll
-          for (int j = 0; j < TN; ++j) tile[dd[j] * VLD + r] = (f16)(acc[i][j][v] * sc[j] + bj[j]);
+          for (int j = 0; j < TN; ++j) tile[(j * 16 + col_l) * VLD + r] = (f16)(acc[i][j][v] * sc[j] + bj[j]);
         }
     } else {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + 8 * (v >> 2) + 4 * grp + (v & 3);
-          const float y0 = acc[i][0][v] * sc[0] + bj[0], y1 = acc[i][1][v] * sc[1] + bj[1];
-          tile[r * QLD + dd[0]] = (f16)(y0 * cA[i][v] - y1 * sA[i][v]);
-          tile[r * QLD + dd[1]] = (f16)(y1 * cA[i][v] + y0 * sA[i][v]);
-          if constexpr (HD == 96) {
-            const float y2 = acc[i][2][v] * sc[2] + bj[2];
-            const float y2p = __shfl_xor(y2, 16);  // partner of the third block
-            tile[r * QLD + dd[2]] = (f16)(col_l < 16 ? y2 * cB[i][v] - y2p * sB[i][v] : y2 * cB[i][v] + y2p * sB[i][v]);
-          } else if constexpr (HD == 128) {
-            const float y2 = acc[i][2][v] * sc[2] + bj[2], y3 = acc[i][3][v] * sc[3] + bj[3];
-            tile[r * QLD + dd[2]] = (f16)(y2 * cB[i][v] - y3 * sB[i][v]);
-            tile[r * QLD + dd[3]] = (f16)(y3 * cB[i][v] + y2 * sB[i][v]);
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * grp + v;
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            const float y0 = acc[i][q][v] * sc[q] + bj[q], y1 = acc[i][q + NP][v] * sc[q + NP] + bj[q + NP];
+            const int d = q * 16 + col_l;
+            tile[r * QLD + d] = (f16)(y0 * cs[i][v][q] - y1 * sn[i][v][q]);
+            tile[r * QLD + d + HALF] = (f16)(y1 * cs[i][v][q] + y0 * sn[i][v][q]);
           }
         }
     }
