@@ -71,7 +71,12 @@ using CfgQL8 = TileCfg<256, 192, 4, 2>;  // 8 waves, wave tile 64 x 96
 using CfgQS8 = TileCfg<128, 192, 4, 2>;  // 8 waves, wave tile 32 x 96
 using CfgQ128 = TileCfg<128, 256, 2, 2>;  // wave tile 64 x 128 (one 128-wide head per wave)
 using CfgQ64 = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64 (one 64-wide head per wave)
-enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64 };
+// QKV below 1024 tokens with as many query as KV heads of width 96: a tile is
+// one Q or K head plus half a V head (144 rows), so the tiles number
+// nh + nkv per 128 tokens (256 at 512 tokens for 32 + 32 heads, one per CU,
+// against 192 of 128 x 192), and move 15% fewer operand bytes each
+using CfgQH = TileCfg<128, 144, 4, 1>;    // wave tile 32 x 144
+enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64, C_QH };
 
 struct GemmPlan {
   int cfg, tiles_m, tiles_n, splits, kpt, group_m;
@@ -92,6 +97,7 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
     case C_QL: bm = 256; bn = 192; break;
     case C_Q128: bm = 128; bn = 256; break;
     case C_Q64: bm = 128; bn = 128; break;
+    case C_QH: bm = 128; bn = 144; break;
     default: bm = 128; bn = 192; break;
   }
 }
@@ -101,11 +107,13 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 // for 256 CUs, so K is split into as many ranges as give one even round of
 // workgroups (any count: 5 at 512 tokens, 240 workgroups of 256 x 128).  int8 and binary16
 // weights share the plans (both go global -> LDS by DMA).
-GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
+GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96, int nh = 0, int nkv = 0) {
   GemmPlan p{};
-  (void)w8;
-  if (epi == EPI_QKV) p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
-  else if (epi == EPI_SILU) p.cfg = M >= 1024 ? C_L : C_M;
+  if (epi == EPI_QKV) {
+    p.cfg = hd == 128 ? C_Q128 : (hd == 64 ? C_Q64 : (M >= 1024 ? C_QL : C_QS));
+    // head-and-a-half tiles when they make one round of at most 256 workgroups
+    if (p.cfg == C_QS && !w8 && nh == nkv && nh > 0 && (long)((M + 127) / 128) * (nh + nkv) <= kCUs) p.cfg = C_QH;
+  } else if (epi == EPI_SILU) p.cfg = M >= 1024 ? C_L : C_M;
   else if (epi == EPI_F32) p.cfg = C_L;
   else {
     // 256 x 192 when the output width divides and it gives whole rounds of
@@ -118,7 +126,7 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96) {
   int bm, bn;
   cfg_dims(p.cfg, bm, bn);
   p.tiles_m = (M + bm - 1) / bm;
-  p.tiles_n = epi == EPI_SILU ? (N / 2) / (bn / 2) : (N + bn - 1) / bn;
+  p.tiles_n = epi == EPI_SILU ? (N / 2) / (bn / 2) : (p.cfg == C_QH ? nh + nkv : (N + bn - 1) / bn);
   const int nk = K / 64;
   int s = 1;
   // residual GEMMs: as many K splits as keep one round of at most 256
@@ -150,11 +158,15 @@ constexpr int gemm_stages() {
 // 1.595 -> 1.49 ms per forward.  Not for the 4-wave QKV tiles (their RoPE
 // factors spill at 256 registers per lane), nor the other 8-wave tiles (the
 // 256 x 192 residual tile spills at 168 registers and measured 19% slower).
+// The 128 x 144 QKV tile gets 2: its 16 + 18 copies per stage split evenly
+// only over two waves.
 template <class C, bool W8, int EPI>
 constexpr int gemm_copy_waves() {
   return ((!W8 && EPI != EPI_QKV && C::NW == 4 && C::WM * C::WN <= 8192) ||
           (!W8 && EPI != EPI_QKV && C::BM == 256 && C::BN == 128 && C::NW == 8) ||
-          (!W8 && EPI == EPI_QKV && C::NW == 8 && C::BM == 128 && C::WN == 96)) ? 4 : 0;
+          (!W8 && EPI == EPI_QKV && C::NW == 8 && C::BM == 128 && C::WN == 96)) ? 4
+         : (!W8 && EPI == EPI_QKV && C::BN == 144) ? 2   // 34 copies per stage: 17 each
+         : 0;
 }
 
 // Kernel launch.  With profiling events (ev non-null) the two events ride on
@@ -180,9 +192,12 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
   using QL = CfgQL8;
   using QS = CfgQS8;
   if constexpr (EPI == EPI_QKV) {
-    if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
-    else if (cfg == C_Q128) launch_mfma<CfgQ128, W8, EPI>(a, st, ev);
-    else if (cfg == C_Q64) launch_mfma<CfgQ64, W8, EPI>(a, st, ev);
+    // the head width picks the kernel family first: a QKV kernel writes Q, K
+    // and V^T with its own head width, so it never runs on another model's
+    if (a.hd == 128) launch_mfma<CfgQ128, W8, EPI>(a, st, ev);
+    else if (a.hd == 64) launch_mfma<CfgQ64, W8, EPI>(a, st, ev);
+    else if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
+    else if (cfg == C_QH && !W8 && a.nh == a.nkv && a.tiles_n == a.nh + a.nkv) launch_mfma<CfgQH, false, EPI>(a, st, ev);
     else launch_mfma<QS, W8, EPI>(a, st, ev);
   } else if constexpr (EPI == EPI_SILU) {
     if (cfg == C_L) launch_mfma<CfgL, W8, EPI>(a, st, ev);
@@ -211,7 +226,7 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.s_pad = (int)round_up((size_t)seq, 64);
   const int H = c.hidden, hd = c.head_dim, I = c.intermediate;
   const bool w8 = c.wtype == PHI_WT_I8;
-  p.qkv = plan_gemm(EPI_QKV, p.T, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8, hd);
+  p.qkv = plan_gemm(EPI_QKV, p.T, (c.n_heads + 2 * c.n_kv_heads) * hd, H, w8, hd, c.n_heads, c.n_kv_heads);
   p.o = plan_gemm(EPI_RESID, p.T, H, c.n_heads * hd, w8);
   p.gu = plan_gemm(EPI_SILU, p.T, 2 * I, H, w8);
   p.down = plan_gemm(EPI_RESID, p.T, H, I, w8);

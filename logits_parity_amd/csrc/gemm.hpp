@@ -94,6 +94,11 @@ __device__ __forceinline__ int w_row_mfma(const GemmArgs& a, int tn, int r) {
     const int blk = r >> 4, p = blk >> 1;
     const int out = tn * (BN / 2) + p * 16 + (r & 15);
     return (blk & 1) ? (a.N >> 1) + out : out;
+  } else if constexpr (EPI == EPI_QKV && BN == 144) {
+    // head-and-a-half tiles: Q or K head tn (96 rows), then V rows 48 (tn % 2) ..
+    // of V head tn / 2 (tiles cover nh + nkv heads with nh = nkv)
+    const int n = r < 96 ? tn * 96 + r : (a.nh + a.nkv) * 96 + tn * 48 + (r - 96);
+    return n < a.N ? n : a.N - 1;
   } else {
     const int n = tn * BN + r;
     return n < a.N ? n : a.N - 1;
@@ -161,8 +166,12 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   constexpr int JMAX = INS_A + INS_W - 1;             // last copy of a stage
   static_assert(LPW * NDW == INS_A + INS_W || VG, "stage split (binary16 DMA tiles divide evenly)");
   static_assert(TM * 16 == WM && TN * 16 == WN, "wave tile");
-  static_assert(EPI != EPI_QKV || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
-  constexpr int HD = EPI == EPI_QKV ? WN : 96;
+  // QH: 144-wide QKV tiles of one Q or K head plus half a V head (head_dim 96,
+  // as many query as KV heads), the whole tile width in every wave
+  constexpr bool QH = EPI == EPI_QKV && BN == 144;
+  static_assert(!QH || WN == 144, "QKV head-and-a-half tile: one wave column");
+  static_assert(EPI != EPI_QKV || QH || WN == 64 || WN == 96 || WN == 128, "QKV: one head (64, 96 or 128 wide) per wave");
+  constexpr int HD = EPI == EPI_QKV ? (QH ? 96 : WN) : 96;
   static_assert(EPI != EPI_SILU || TN % 2 == 0, "SILU: gate/up block pairs");
 
   // the QKV epilogue stages each wave's head tile in the same LDS
@@ -461,6 +470,104 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
           if (m >= a.M) continue;
           act[(size_t)m * a.ld_act + n] = (f16)silu_mul(acc[i][2 * p][v] * sc[2 * p], acc[i][2 * p + 1][v] * sc[2 * p + 1]);
         }
+    }
+  } else if constexpr (QH) {
+    // Q or K head tn with RoPE (blocks 0..5, partners j and j + 3), then V^T
+    // dims 48 (tn % 2) .. + 48 of V head tn / 2 (blocks 6..8); each part goes
+    // through the wave's LDS region and leaves as 16-byte stores
+    constexpr int HALF = 48, NP = 3;
+    constexpr int QLD = HD + 8, VLD = WM + 8;
+    constexpr int REG = QKV_REG;
+    static_assert(WM * QLD <= REG && HALF * VLD <= REG && NW * REG <= SMEM, "QKV staging");
+    const bool is_q = tn < a.nh;
+    const int head = is_q ? tn : tn - a.nh, nheads = is_q ? a.nh : a.nkv;
+    const int vh = tn >> 1, vd0 = (tn & 1) * HALF;
+    const int mw0 = m0 + wm * WM;
+    float cs[TM][4][NP], sn[TM][4][NP];
+    {
+      const int s_base = mw0 - (mw0 / a.S) * a.S;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * grp + v;
+          int sp;
+          if (a.pos) {
+            sp = a.pos[min(mw0 + r, a.M - 1)];
+            sp = sp < 0 ? 0 : (sp >= a.max_pos ? a.max_pos - 1 : sp);
+          } else {
+            sp = s_base + r;
+            while (sp >= a.S) sp -= a.S;
+          }
+          const size_t t = (size_t)sp * HALF;
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            cs[i][v][q] = a.rope_cos[t + q * 16 + col_l];
+            sn[i][v][q] = a.rope_sin[t + q * 16 + col_l];
+          }
+        }
+    }
+    float bj[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bj[j] = a.bias ? (float)a.bias[w_row_mfma<EPI, BN>(a, tn, j * 16 + col_l)] : 0.f;
+    __syncthreads();                      // every wave is done with the k-stages
+    f16* tile = smem + wave * REG;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = i * 16 + 4 * grp + v;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          const float y0 = acc[i][q][v] * sc[q] + bj[q], y1 = acc[i][q + NP][v] * sc[q + NP] + bj[q + NP];
+          const int d = q * 16 + col_l;
+          tile[r * QLD + d] = (f16)(y0 * cs[i][v][q] - y1 * sn[i][v][q]);
+          tile[r * QLD + d + HALF] = (f16)(y1 * cs[i][v][q] + y0 * sn[i][v][q]);
+        }
+      }
+    // the wave reads back only what it wrote: its own LDS operations are ordered
+    {
+      f16* dst = reinterpret_cast<f16*>(is_q ? a.q : a.k);
+      constexpr int CR = HD / 8;
+      for (int idx = lane; idx < WM * CR; idx += 64) {
+        const int r = idx / CR, c = idx - r * CR;
+        const int m = mw0 + r;
+        if (m >= a.M) continue;
+        const int b = m / a.S, s = m - b * a.S;
+        *reinterpret_cast<f16x8*>(dst + ((size_t)(b * nheads + head) * a.S + s) * HD + c * 8) =
+            *reinterpret_cast<const f16x8*>(tile + r * QLD + c * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = i * 16 + 4 * grp + v;
+#pragma unroll
+        for (int j = 2 * NP; j < TN; ++j) tile[((j - 2 * NP) * 16 + col_l) * VLD + r] = (f16)(acc[i][j][v] * sc[j] + bj[j]);
+      }
+    {
+      f16* vt = reinterpret_cast<f16*>(a.vt);
+      constexpr int CPR = WM / 8;  // 8-token chunks per V^T row segment
+      const bool aligned = (a.S & 7) == 0 && (a.s_pad & 7) == 0;
+      for (int idx = lane; idx < HALF * CPR; idx += 64) {
+        const int dl = idx / CPR, c = idx - dl * CPR;
+        const int d = vd0 + dl;
+        const int m = mw0 + c * 8;
+        if (m >= a.M) continue;
+        if (aligned) {
+          const int b = m / a.S, s = m - b * a.S;
+          *reinterpret_cast<f16x8*>(vt + ((size_t)(b * a.nkv + vh) * HD + d) * a.s_pad + s) =
+              *reinterpret_cast<const f16x8*>(tile + dl * VLD + c * 8);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (m + e >= a.M) break;
+            const int b = (m + e) / a.S, s = m + e - b * a.S;
+            vt[((size_t)(b * a.nkv + vh) * HD + d) * a.s_pad + s] = tile[dl * VLD + c * 8 + e];
+          }
+        }
+      }
     }
   } else {  // EPI_QKV
     // RoPE on the accumulators, then the wave's WM x HD head tile goes through

@@ -180,6 +180,22 @@ def test_mini_one_layer_ragged_1100_vs_oracle(phi):
     _gate(got, ref)
 
 
+@pytest.mark.parametrize("batch,seq", [(1, 300), (3, 101)])
+def test_mini_one_layer_head_and_a_half_qkv_vs_oracle(phi, batch, seq):
+    """Full Phi-3-mini width, one layer, under 1024 tokens: QKV on 128 x 144
+    tiles (one Q or K head plus half a V head each, nh + nkv = 64 tiles per
+    128 tokens), with a ragged last M-tile; at S = 101 the V^T rows leave
+    through the unaligned store path (8-token chunks straddle sequences)."""
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.MINI, n_layers=1)
+    _say(f"mini 1 layer {batch}x{seq}")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, batch, seq)
+    got = _run(phi, cfg, to_device(ws, 1, "cuda"), ids)
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    _gate(got, ref)
+
+
 def test_mini_w8_one_layer_ragged_1100_vs_oracle(phi):
     """The same shape with int8 weights against the oracle on those weights:
     the 8-wave 256 x 192 QKV tile (44 register-staged copies per stage padded
