@@ -363,6 +363,8 @@ phi_status norm(bool embed, NormArgs a, hipStream_t st, const hipEvent_t* ev = n
 #define PHI_NORM_CASE(CH)                                                                                      \
   case CH:                                                                                                     \
     if (embed) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, true, CH>), dim3(a.T), dim3(kNormThreads), st, a);       \
+    else if (a.nsplit == 0) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH, 0>), dim3(a.T), dim3(kNormThreads), st, a); \
+    else if (a.nsplit == 5) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH, 5>), dim3(a.T), dim3(kNormThreads), st, a); \
     else PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH>), dim3(a.T), dim3(kNormThreads), st, a);            \
     break;
     PHI_NORM_CASE(1) PHI_NORM_CASE(2) PHI_NORM_CASE(3) PHI_NORM_CASE(4)
