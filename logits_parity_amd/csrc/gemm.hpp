@@ -11,17 +11,20 @@
 //    the shader-cycle and 100 MHz counters inside the kernel) and faster.
 //  - K is walked in steps of 64 through a ring of NS LDS stages, NS - 1 of
 //    them in flight while one is consumed, so the DMA of a k-step has NS - 1
-//    k-steps of MFMA work to arrive.  Operands go global -> LDS directly
-//    (buffer_load_dwordx4 ... lds, no VGPR staging): one wave instruction fills
-//    1 KB = 8 binary16 rows of 128 B, or 16 int8 weight rows of 64 B.  int8
-//    codes are widened exactly to binary16 (|q| <= 127) as their fragments
-//    are read from LDS; the per-row scale multiplies the fp32 accumulator (it
-//    factors out of the K sum).
+//    k-steps of MFMA work to arrive.  binary16 operands go global -> LDS
+//    directly (buffer_load_dwordx4 ... lds, no VGPR staging): one wave
+//    instruction fills 1 KB = 8 rows of 128 B.  int8 weights are staged
+//    through registers (16 codes per lane and load) and widened exactly to
+//    binary16 (|q| <= 127) as they are written to LDS, once per element, so
+//    both weight types share one LDS layout (the 256 x 256 tiles, short of
+//    registers for that, keep codes in LDS and widen B fragments as they are
+//    read); the per-row scale multiplies the fp32 accumulator (it factors out
+//    of the K sum).
 //  - Rows are stored with an XOR swizzle of their 16-byte chunks,
 //    chunk' = chunk ^ ((row >> 1) & 7): 16 lanes reading 16 consecutive rows
 //    at one logical chunk touch 16 distinct 16-byte bank groups of the
-//    256-byte LDS bank row, so fragment reads are conflict free (int8 rows:
-//    chunk' = chunk ^ ((row >> 1) & 3) over their four chunks).
+//    256-byte LDS bank row, so fragment reads are conflict free (int8 code
+//    rows: chunk' = chunk ^ ((row >> 1) & 3) over their four chunks).
 //  - A k-step is two k32 sub-steps.  The reads for sub-step s + 1 run behind
 //    the MFMAs of sub-step s: the operand with more blocks per wave is
 //    streamed (block o of the next sub-step is read into the registers of
@@ -142,18 +145,30 @@ struct TileCfg {
 // each), so copies issued by the compute waves leave their MFMA pipes idle.
 template <class C, bool W8, int EPI, int NS, int HW = 0>
 __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs a) {
-  // int8 weights take the register-staged copy (measured faster for their
-  // 64-byte rows); binary16 operands go global -> LDS by DMA
+  // int8 weights take the register-staged copy (their 64-byte rows measured
+  // faster that way, and the registers are where they are widened);
+  // binary16 operands go global -> LDS by DMA
   constexpr bool VG = W8;
+  static_assert(!W8 || VG, "int8 codes are widened on their way into LDS (register staging only)");
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, TM = C::TM, TN = C::TN;
   constexpr int NT = C::NT, NW = C::NW, BK = 64;
   static_assert(NS >= 2 && NS <= 4, "stages");
-  // An LDS stage holds A [BM][64] binary16 (128-byte rows, eight 16-byte
-  // chunks) then W [BN][64]: binary16 (128-byte rows), or int8 codes
-  // (64-byte rows, four 16-byte chunks) widened to binary16 when fragments
-  // are read.  Both go global -> LDS by DMA, 1 KB per wave instruction.
-  constexpr int WB = W8 ? 1 : 2;                     // bytes per weight element
-  constexpr int STAGE = (BM * BK * 2 + BN * BK * WB) / 2;  // f16 elements per LDS stage
+  // An LDS stage holds A [BM][64] then W [BN][64], binary16 with 128-byte
+  // rows of eight 16-byte chunks (or int8 codes in 64-byte rows, see WIDEN).
+  // A copy instruction moves 1 KB from HBM: 8 binary16 rows, or 16 rows of
+  // int8 codes (64 bytes each).
+  constexpr int WB = W8 ? 1 : 2;                     // bytes per weight element in HBM
+  // WIDEN: int8 codes are widened to binary16 once, as their registers are
+  // written to LDS, and share the binary16 LDS layout.  The 256 x 256 tiles
+  // keep them as codes in LDS (64-byte rows, chunk' = chunk ^ ((row >> 1) & 3))
+  // and widen them as fragments are read: widening on the way in spills
+  // there (128 bytes per lane; gate/up at 4 x 1024 13.9 -> 19.3 ms per
+  // forward), while on the 256 x 192 tiles it took QKV 9.36 -> 8.38, o_proj
+  // 3.75 -> 3.48 and down 8.26 -> 7.42 ms (each B fragment was widened by
+  // every wave of its column before).
+  constexpr bool WIDEN = W8 && !(BM == 256 && BN == 256);
+  constexpr int WLB = W8 && !WIDEN ? 1 : 2;          // bytes per weight element in LDS
+  constexpr int STAGE = (BM * BK * 2 + BN * BK * WLB) / 2;  // f16 elements per LDS stage
   constexpr int INS_A = BM * 8 / 64;                 // 1 KB DMA instructions for A per stage
   constexpr int INS_W = BN * BK * WB / 1024;
   static_assert(HW == 0 || !VG, "copy waves only on the DMA path");
@@ -218,7 +233,12 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     if (!is_w) {
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
       src_off[t] = (m0 + r < a.M ? m0 + r : a.M - 1) * K + c * 8;
+    } else if constexpr (WIDEN) {
+      // 16 codes (k = 16 c4 .. + 15) of row r; swizzled when written to LDS
+      const int sw = s - INS_A * 64, r = sw >> 2, c4 = sw & 3;
+      src_off[t] = w_row_mfma<EPI, BN>(a, tn, r) * K + c4 * 16;
     } else if constexpr (W8) {
+      // the slot's swizzled 16-code chunk of row r (codes stay codes in LDS)
       const int sw = s - INS_A * 64, r = sw >> 2, c = (sw & 3) ^ ((r >> 1) & 3);
       src_off[t] = w_row_mfma<EPI, BN>(a, tn, r) * K + c * 16;
     } else {
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   };
   auto ldB = [&](const f16* cur, int kk, int j) __attribute__((always_inline)) -> f16x8 {
     const int r = wn * WN + j * 16 + (lane & 15);
-    if constexpr (W8) {
+    if constexpr (W8 && !WIDEN) {
       // the lane's 8 codes: 16-code chunk 2 kk + g / 2, half g % 2 (g = l / 16)
       const uint8_t* curw = reinterpret_cast<const uint8_t*>(cur + BM * BK);
       const int g = lane >> 4;
@@ -350,8 +370,21 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     };
     auto lput = [&](f16* st, const i32x4* r) {
 #pragma unroll
-      for (int t = 0; t < LPW; ++t)
-        *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(st) + (PAD ? min(wave + NW * t, JMAX) : wave + NW * t) * 1024 + 16 * lane) = r[t];
+      for (int t = 0; t < LPW; ++t) {
+        const int j = PAD ? min(wave + NW * t, JMAX) : wave + NW * t;
+        if (!WIDEN || t < TA_) {
+          *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(st) + j * 1024 + 16 * lane) = r[t];
+        } else {
+          // 16 int8 codes of row rw -> binary16 chunks 2 c4 and 2 c4 + 1 of
+          // its 128-byte LDS row (the binary16 layout and swizzle)
+          const int sw = (j - INS_A) * 64 + lane, rw = sw >> 2, c4 = sw & 3;
+          const f16x8 h0 = i8x8_to_f16x8((uint32_t)r[t][0], (uint32_t)r[t][1]);
+          const f16x8 h1 = i8x8_to_f16x8((uint32_t)r[t][2], (uint32_t)r[t][3]);
+          f16* wrow = st + BM * BK;
+          *reinterpret_cast<f16x8*>(wrow + swz(rw, 2 * c4)) = h0;
+          *reinterpret_cast<f16x8*>(wrow + swz(rw, 2 * c4 + 1)) = h1;
+        }
+      }
     };
     if (kt0 < kt1) {
       gload(kt0, r0);
