@@ -242,7 +242,7 @@ PrefillPlan plan_prefill(const phi_config& c, int batch, int seq) {
   p.off_attn = take(T * c.n_heads * hd * as);
   p.off_act = take(T * (size_t)I * as);
   const int max_split = c.wtype == PHI_WT_F32 ? 0 : std::max(p.o.splits, p.down.splits);
-  p.off_part = take(max_split > 1 ? (size_t)max_split * T * H * 4 : 0);
+  p.off_part = take(max_split > 1 ? (size_t)max_split * T * H * 2 : 0);  // binary16 partials
   p.off_ids = take(T * 4);  // the device copy of host ids (phi_prefill_logits_host_ids)
   p.total = o;
   return p;
@@ -445,7 +445,7 @@ phi_status forward(const phi_model* m, const int32_t* ids, int batch, int seq, f
   na.embed = m->embed;
   na.x = x;
   na.xn = xn;
-  na.part = part;
+  na.part = reinterpret_cast<const f16*>(part);
   na.T = T;
   na.H = H;
   na.V = c.vocab;
@@ -694,7 +694,7 @@ DecodeStepPlan plan_decode_step(const phi_config& c, int batch, int max_ctx) {
   p.off_attn = take((size_t)B * c.n_heads * hd * 2);
   p.off_act = take((size_t)B * I * 2);
   const int max_split = std::max(p.o.splits, p.down.splits);
-  p.off_part = take(max_split > 1 ? (size_t)max_split * B * H * 4 : 0);
+  p.off_part = take(max_split > 1 ? (size_t)max_split * B * H * 2 : 0);  // binary16 partials
   p.off_ctx = take((size_t)B * 4);
   p.off_att = take(p.att.total);
   p.total = o;
@@ -729,7 +729,7 @@ phi_status decode_step(const phi_model* m, const int32_t* ids, const int32_t* po
   na.embed = m->embed;
   na.x = x;
   na.xn = xn;
-  na.part = part;
+  na.part = reinterpret_cast<const f16*>(part);
   na.T = B;
   na.H = H;
   na.V = c.vocab;

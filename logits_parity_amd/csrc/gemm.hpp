@@ -42,7 +42,8 @@
 // column l % 16 and rows 4 (l / 16) + v, v < 4):
 //  EPI_F32      logits: out[m][n] = acc
 //  EPI_RESID    residual: x[m][n] += acc
-//  EPI_PARTIAL  split-K: part[split][m][n] = acc
+//  EPI_PARTIAL  split-K: part[split][m][n] = acc, binary16 (staged through LDS
+//               for full-line stores)
 //  EPI_SILU     fused gate/up: the tile reads weight rows in 16-row blocks
 //               alternating gate, up for the same outputs, so a lane holds
 //               gate and up of one output: act = silu(gate) * up
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
 
   // ---------------------------------------------------------------- epilogue
   if (HW > 0 && wave >= NW) {
-    if constexpr (EPI == EPI_QKV) __syncthreads();  // the one barrier of the QKV epilogue
+    if constexpr (EPI == EPI_QKV || EPI == EPI_PARTIAL) __syncthreads();  // the one barrier of the epilogue
     return;
   }
   const int grp = lane >> 4, col_l = lane & 15;
@@ -473,7 +474,37 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     if constexpr (W8) sc[j] = (float)reinterpret_cast<const f16*>(a.scale)[w_row_mfma<EPI, BN>(a, tn, wn * WN + j * 16 + col_l)];
   }
 
-  if constexpr (EPI == EPI_F32 || EPI == EPI_RESID || EPI == EPI_PARTIAL) {
+  if constexpr (EPI == EPI_PARTIAL) {
+    // binary16 partial tile: staged through the wave's own LDS rows, 16 rows
+    // at a time, then stored as 8-byte vectors (16 lanes write one 128-byte
+    // row segment of 64 columns)
+    constexpr int SLD = WN + 4;  // staging row stride (floats)
+    static_assert(NW * 16 * SLD * 4 <= SMEM * 2, "partial staging fits");
+    __syncthreads();  // every wave is done with the k-stages
+    float* stg = reinterpret_cast<float*>(smem) + wave * 16 * SLD;
+    f16* po = reinterpret_cast<f16*>(a.out);
+    const int n0 = tn * BN + wn * WN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) stg[(4 * grp + v) * SLD + j * 16 + col_l] = acc[i][j][v] * sc[j];
+      constexpr int CPR = WN / 4;  // 4-column chunks per row
+#pragma unroll
+      for (int idx = lane; idx < 16 * CPR; idx += 64) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int m = m0 + wm * WM + i * 16 + r, n = n0 + 4 * c;
+        f32x4 y = *reinterpret_cast<const f32x4*>(stg + r * SLD + 4 * c);
+        // saturate instead of overflowing to inf (a partial of a finite sum
+        // beyond the binary16 range is not expected on real activations); a
+        // NaN stays NaN, so bad rows still come out NaN
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = y[e] > 65504.f ? 65504.f : (y[e] < -65504.f ? -65504.f : y[e]);
+        if (m < a.M && n < a.N) vec4<f16>::store(po + ((size_t)split * a.M + m) * a.N + n, y);
+      }
+    }
+  } else if constexpr (EPI == EPI_F32 || EPI == EPI_RESID) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int n = tn * BN + wn * WN + j * 16 + col_l;
@@ -486,8 +517,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
           if (m >= a.M) continue;
           const float y = acc[i][j][v] * sc[j];
           if constexpr (EPI == EPI_F32) a.out[(size_t)m * a.ldo + n] = y;
-          else if constexpr (EPI == EPI_RESID) a.x[(size_t)m * a.ldx + n] += y;
-          else a.out[((size_t)split * a.M + m) * a.N + n] = y;
+          else a.x[(size_t)m * a.ldx + n] += y;
         }
     }
   } else if constexpr (EPI == EPI_SILU) {

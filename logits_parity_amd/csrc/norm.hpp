@@ -3,7 +3,7 @@
 // RMSNorm: xn = x / sqrt(mean(x^2) + eps) * g over the hidden axis, with the
 // fp32 residual row x as input and the GEMM input type as output.  One
 // workgroup per row; sums in fp32.  When the preceding residual GEMM was split over K,
-// its nsplit fp32 partials are first added to x in split order (a fixed
+// its nsplit binary16 partials are first added to x in split order (a fixed
 // order, so the result does not depend on scheduling) and x is written back.
 #pragma once
 #include "common.hpp"
@@ -16,7 +16,7 @@ struct NormArgs {
   float* x;            // [T][H] residual, fp32
   const void* gain;    // [H]
   void* xn;            // [T][H] output (AT)
-  const float* part;   // [nsplit][T][H] partial sums to add to x first (nsplit > 0)
+  const f16* part;     // [nsplit][T][H] binary16 partial sums to add to x first (nsplit > 0)
   int nsplit;
   int T, H, V;
   float eps;
@@ -85,14 +85,14 @@ __global__ __launch_bounds__(kNormThreads) void phi_norm_kernel(NormArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) v[i] = vec4<float>::load(xr + col[i]);
     if (NSP != 0 && a.nsplit > 0) {
-      const float* pr = a.part + (size_t)row * a.H;
+      const f16* pr = a.part + (size_t)row * a.H;
       const size_t plane = (size_t)a.T * a.H;
       if constexpr (NSP > 0) {
         f32x4 pv[NSP > 0 ? NSP : 1][CH];
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
-          for (int i = 0; i < CH; ++i) pv[sp][i] = vec4<float>::load(pr + sp * plane + col[i]);
+          for (int i = 0; i < CH; ++i) pv[sp][i] = vec4<f16>::load(pr + sp * plane + col[i]);
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kNormThreads) void phi_norm_kernel(NormArgs a) {
 #pragma unroll 4
         for (int sp = 0; sp < a.nsplit; ++sp)
 #pragma unroll
-          for (int i = 0; i < CH; ++i) v[i] += vec4<float>::load(pr + sp * plane + col[i]);
+          for (int i = 0; i < CH; ++i) v[i] += vec4<f16>::load(pr + sp * plane + col[i]);
       }
 #pragma unroll
       for (int i = 0; i < CH; ++i)
