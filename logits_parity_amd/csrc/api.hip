@@ -106,7 +106,8 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 // per MFMA low; at small M the residual GEMMs (N = hidden) have too few tiles
 // for 256 CUs, so K is split into as many ranges as give one even round of
 // workgroups (any count: 5 at 512 tokens, 240 workgroups of 256 x 128).  int8 and binary16
-// weights share the plans (both go global -> LDS by DMA).
+// weights share the plans (binary16 copies go global -> LDS by DMA, int8
+// through registers), except the head-and-a-half QKV tiles (binary16 only).
 GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96, int nh = 0, int nkv = 0) {
   GemmPlan p{};
   if (epi == EPI_QKV) {
