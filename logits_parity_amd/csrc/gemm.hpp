@@ -484,19 +484,41 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     // lm_head 0.74 -> 0.70 ms per forward.
     constexpr int SLD = WN + 4;  // staging row stride (floats)
     static_assert(NW * 16 * SLD * 4 <= SMEM * 2, "epilogue staging fits");
-    __syncthreads();  // every wave is done with the k-stages
+    constexpr int CPR = WN / 4;         // 4-column chunks per row
+    constexpr int NQ = 16 * CPR / 64;   // chunks per lane per 16-row block
+    static_assert(16 * CPR % 64 == 0, "whole chunks per lane");
+    const int n0 = tn * BN + wn * WN;
+    // The residual rows of the wave's tile are loaded before the staging
+    // barrier, all in flight at once.  Loaded next to its store, each
+    // load-add-store waited for its own load (the compiler cannot prove a
+    // store and the next load apart): one memory latency per 4 columns.
+    f32x4 xres[EPI == EPI_RESID ? TM : 1][EPI == EPI_RESID ? NQ : 1];
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int idx = lane + 64 * q, r = idx / CPR, c = idx - r * CPR;
+          const int m = m0 + wm * WM + i * 16 + r, n = n0 + 4 * c;
+          // (clamped into the tile's valid rows and columns instead of a
+          // branch per load; the store below keeps the bounds check)
+          xres[i][q] = vec4<float>::load(a.x + (size_t)min(m, a.M - 1) * a.ldx + min(n, a.N - 4));
+        }
+      lds_barrier();  // every wave is done with the k-stages (LDS only: the loads stay in flight)
+    } else {
+      __syncthreads();  // every wave is done with the k-stages
+    }
     float* stg = reinterpret_cast<float*>(smem) + wave * 16 * SLD;
     f16* po = reinterpret_cast<f16*>(a.out);
-    const int n0 = tn * BN + wn * WN;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) stg[(4 * grp + v) * SLD + j * 16 + col_l] = acc[i][j][v] * sc[j];
-      constexpr int CPR = WN / 4;  // 4-column chunks per row
 #pragma unroll
-      for (int idx = lane; idx < 16 * CPR; idx += 64) {
+      for (int q = 0; q < NQ; ++q) {
+        const int idx = lane + 64 * q;
         const int r = idx / CPR, c = idx - r * CPR;
         const int m = m0 + wm * WM + i * 16 + r, n = n0 + 4 * c;
         f32x4 y = *reinterpret_cast<const f32x4*>(stg + r * SLD + 4 * c);
@@ -510,7 +532,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
         if (m < a.M && n < a.N) {
           if constexpr (EPI == EPI_PARTIAL) vec4<f16>::store(po + ((size_t)split * a.M + m) * a.N + n, y);
           else if constexpr (EPI == EPI_F32) vec4<float>::store(a.out + (size_t)m * a.ldo + n, y);
-          else { float* px = a.x + (size_t)m * a.ldx + n; vec4<float>::store(px, vec4<float>::load(px) + y); }
+          else vec4<float>::store(a.x + (size_t)m * a.ldx + n, xres[EPI == EPI_RESID ? i : 0][EPI == EPI_RESID ? q : 0] + y);
         }
       }
     }
