@@ -277,6 +277,39 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{};
+  // QH: the compute waves load the RoPE factors of their rows (position of
+  // row 4 (l / 16) + v of each 16-row block, dims l % 16 + 16 q of the 48
+  // pairs) before the main loop, so that the last wave to finish it does not
+  // wait for them after the final barrier (QKV 1.212 -> 1.198 ms per forward
+  // at 1 x 512); the other QKV tiles have no registers to spare for them
+  float qh_cs[QH ? TM : 1][4][3], qh_sn[QH ? TM : 1][4][3];
+  if constexpr (QH) {
+    if (HW == 0 || !copies) {
+      const int grp0 = lane >> 4, col0 = lane & 15;
+      const int mw0 = m0 + wm * WM;
+      const int s_base = mw0 - (mw0 / a.S) * a.S;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * grp0 + v;
+          int sp;
+          if (a.pos) {
+            sp = a.pos[min(mw0 + r, a.M - 1)];
+            sp = sp < 0 ? 0 : (sp >= a.max_pos ? a.max_pos - 1 : sp);
+          } else {
+            sp = s_base + r;
+            while (sp >= a.S) sp -= a.S;
+          }
+          const size_t t = (size_t)sp * 48;
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            qh_cs[i][v][q] = a.rope_cos[t + q * 16 + col0];
+            qh_sn[i][v][q] = a.rope_sin[t + q * 16 + col0];
+          }
+        }
+    }
+  }
 
   // Fragments of k32 sub-step kk (k = 32 kk .. 32 kk + 31 of the stage): A
   // block i is 16 rows x 32 k, B block j 16 columns x 32 k; lane l holds row
@@ -562,30 +595,7 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
     const int head = is_q ? tn : tn - a.nh, nheads = is_q ? a.nh : a.nkv;
     const int vh = tn >> 1, vd0 = (tn & 1) * HALF;
     const int mw0 = m0 + wm * WM;
-    float cs[TM][4][NP], sn[TM][4][NP];
-    {
-      const int s_base = mw0 - (mw0 / a.S) * a.S;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = i * 16 + 4 * grp + v;
-          int sp;
-          if (a.pos) {
-            sp = a.pos[min(mw0 + r, a.M - 1)];
-            sp = sp < 0 ? 0 : (sp >= a.max_pos ? a.max_pos - 1 : sp);
-          } else {
-            sp = s_base + r;
-            while (sp >= a.S) sp -= a.S;
-          }
-          const size_t t = (size_t)sp * HALF;
-#pragma unroll
-          for (int q = 0; q < NP; ++q) {
-            cs[i][v][q] = a.rope_cos[t + q * 16 + col_l];
-            sn[i][v][q] = a.rope_sin[t + q * 16 + col_l];
-          }
-        }
-    }
+    static_assert(HALF == 48 && NP == 3, "RoPE factors loaded before the main loop");
     float bj[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) bj[j] = a.bias ? (float)a.bias[w_row_mfma<EPI, BN>(a, tn, j * 16 + col_l)] : 0.f;
@@ -600,8 +610,8 @@ __global__ __launch_bounds__(C::NT + 64 * HW) void phi_gemm_mfma_kernel(GemmArgs
         for (int q = 0; q < NP; ++q) {
           const float y0 = acc[i][q][v] * sc[q] + bj[q], y1 = acc[i][q + NP][v] * sc[q + NP] + bj[q + NP];
           const int d = q * 16 + col_l;
-          tile[r * QLD + d] = (f16)(y0 * cs[i][v][q] - y1 * sn[i][v][q]);
-          tile[r * QLD + d + HALF] = (f16)(y1 * cs[i][v][q] + y0 * sn[i][v][q]);
+          tile[r * QLD + d] = (f16)(y0 * qh_cs[i][v][q] - y1 * qh_sn[i][v][q]);
+          tile[r * QLD + d + HALF] = (f16)(y1 * qh_cs[i][v][q] + y0 * qh_sn[i][v][q]);
         }
       }
     // the wave reads back only what it wrote: its own LDS operations are ordered
