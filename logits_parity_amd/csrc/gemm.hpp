@@ -32,23 +32,25 @@
 //    and scheduling barriers keep the compiler from re-serialising them.  The
 //    stage barrier of k-step kt + 1 sits between the two sub-steps of kt, so
 //    the next stage's first reads also run under MFMAs.
-//  - Split-K: a launch may cut K into `splits` ranges; each writes an fp32
-//    partial tile that the next kernel (the residual + RMSNorm) reduces in a
-//    fixed order, so results do not depend on scheduling.
+//  - Split-K: a launch may cut K into `splits` ranges; each writes a binary16
+//    partial tile (saturating, NaN kept) that the next kernel (the residual +
+//    RMSNorm) sums into the fp32 residual in a fixed order, so results do not
+//    depend on scheduling.
 //  - Workgroups map to tiles so that consecutive tiles of one weight column
 //    block run on the same XCD (workgroups go round-robin over the 8 XCDs),
 //    sharing that XCD's L2 for the weight tile.
 // Epilogues work on the accumulator registers (lane l of a 16x16 block holds
 // column l % 16 and rows 4 (l / 16) + v, v < 4):
 //  EPI_F32      logits: out[m][n] = acc
-//  EPI_RESID    residual: x[m][n] += acc
+//  EPI_RESID    residual: x[m][n] += acc (fp32, staged through LDS)
 //  EPI_PARTIAL  split-K: part[split][m][n] = acc, binary16 (staged through LDS
 //               for full-line stores)
 //  EPI_SILU     fused gate/up: the tile reads weight rows in 16-row blocks
 //               alternating gate, up for the same outputs, so a lane holds
 //               gate and up of one output: act = silu(gate) * up
-//  EPI_QKV      fused Q/K/V, one head (64, 96 or 128 wide) per wave, plus an
-//               optional per-row bias before RoPE.  With 16-wide blocks in
+//  EPI_QKV      fused Q/K/V, one head (64, 96 or 128 wide) per wave (or, on
+//               the 128 x 144 tiles, one Q or K head of 96 plus half a V
+//               head per tile), plus an optional per-row bias before RoPE.  With 16-wide blocks in
 //               natural d order, RoPE partners (d, d + HD / 2) sit in blocks
 //               j and j + HD / 32 of the same lane.  The RoPE position is the
 //               row's index within its sequence, or a per-row position
