@@ -76,7 +76,8 @@ using CfgQ64 = TileCfg<128, 128, 2, 2>;   // wave tile 64 x 64 (one 64-wide head
 // nh + nkv per 128 tokens (256 at 512 tokens for 32 + 32 heads, one per CU,
 // against 192 of 128 x 192), and move 15% fewer operand bytes each
 using CfgQH = TileCfg<128, 144, 4, 1>;    // wave tile 32 x 144
-enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64, C_QH };
+using CfgR96 = TileCfg<256, 96, 4, 2>;    // wave tile 64 x 48 (short split-K residual GEMMs)
+enum CfgId { C_L, C_M, C_S, C_QL, C_QS, C_Q128, C_Q64, C_QH, C_R96 };
 
 struct GemmPlan {
   int cfg, tiles_m, tiles_n, splits, kpt, group_m;
@@ -98,6 +99,7 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
     case C_Q128: bm = 128; bn = 256; break;
     case C_Q64: bm = 128; bn = 128; break;
     case C_QH: bm = 128; bn = 144; break;
+    case C_R96: bm = 256; bn = 96; break;
     default: bm = 128; bn = 192; break;
   }
 }
@@ -105,9 +107,11 @@ inline void cfg_dims(int cfg, int& bm, int& bn) {
 // Tile shape per GEMM role and token count: large wave tiles keep LDS traffic
 // per MFMA low; at small M the residual GEMMs (N = hidden) have too few tiles
 // for 256 CUs, so K is split into as many ranges as give one even round of
-// workgroups (any count: 5 at 512 tokens, 240 workgroups of 256 x 128).  int8 and binary16
+// workgroups (any count: at 512 tokens down takes 5, 240 workgroups of
+// 256 x 128, and o_proj 4, 256 workgroups of 256 x 96).  int8 and binary16
 // weights share the plans (binary16 copies go global -> LDS by DMA, int8
-// through registers), except the head-and-a-half QKV tiles (binary16 only).
+// through registers), except the head-and-a-half QKV tiles and the 256 x 96
+// residual tiles (binary16 only, as measured).
 GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96, int nh = 0, int nkv = 0) {
   GemmPlan p{};
   if (epi == EPI_QKV) {
@@ -123,6 +127,18 @@ GemmPlan plan_gemm(int epi, int M, int N, int K, bool w8, int hd = 96, int nh = 
     p.cfg = C_M;
     const long t192 = (long)((M + 255) / 256) * (N / 192);
     if (N % 192 == 0 && t192 >= kCUs && t192 % kCUs == 0) p.cfg = C_QL;
+    else if (!w8 && N % 96 == 0) {
+      // K ranges shorter than 16 k-steps (o_proj at 512 tokens: 9.6 k-steps
+      // on 240 workgroups of 256 x 128) lose more to each range's pipeline
+      // fill and drain than 256 x 96 tiles lose to their 22% more operand
+      // bytes per flop; those give one full round (4 splits of 64 tiles, 12
+      // k-steps each at 512 tokens).  Measured per forward at 1 x 512:
+      // o_proj 0.540 -> 0.505 ms; down (25.6 k-steps) keeps 256 x 128,
+      // where 256 x 96 measured 0.943 -> 0.968 ms.
+      const int tm = (M + 255) / 256, nk = K / 64;
+      const int s128 = std::max(1, std::min(kCUs / (tm * ((N + 127) / 128)), nk / 4));
+      if (s128 > 1 && nk / s128 < 16) p.cfg = C_R96;
+    }
   }
   int bm, bn;
   cfg_dims(p.cfg, bm, bn);
@@ -154,7 +170,7 @@ constexpr int gemm_stages() {
 // Copy waves (4 extra waves that issue all global -> LDS copies) for the
 // binary16 4-wave tiles of at most 128 x 64 per wave (measured 5% faster
 // on the gate/up and residual GEMMs at 512 tokens), the 8-wave 256 x 128
-// tile, and the 8-wave
+// and 256 x 96 tiles, and the 8-wave
 // 128 x 192 QKV tile (144 registers, so 12 waves fit): QKV at 512 tokens
 // 1.595 -> 1.49 ms per forward.  Not for the 4-wave QKV tiles (their RoPE
 // factors spill at 256 registers per lane), nor the other 8-wave tiles (the
@@ -164,7 +180,7 @@ constexpr int gemm_stages() {
 template <class C, bool W8, int EPI>
 constexpr int gemm_copy_waves() {
   return ((!W8 && EPI != EPI_QKV && C::NW == 4 && C::WM * C::WN <= 8192) ||
-          (!W8 && EPI != EPI_QKV && C::BM == 256 && C::BN == 128 && C::NW == 8) ||
+          (!W8 && EPI != EPI_QKV && C::BM == 256 && (C::BN == 128 || C::BN == 96) && C::NW == 8) ||
           (!W8 && EPI == EPI_QKV && C::NW == 8 && C::BM == 128 && C::WN == 96)) ? 4
          : (!W8 && EPI == EPI_QKV && C::BN == 144) ? 2   // 34 copies per stage: 17 each
          : 0;
@@ -207,6 +223,7 @@ void launch_cfg(int cfg, GemmArgs a, hipStream_t st, const hipEvent_t* ev) {
     launch_mfma<CfgL, W8, EPI>(a, st, ev);
   } else {
     if (cfg == C_M) launch_mfma<CfgM, W8, EPI>(a, st, ev);
+    else if (cfg == C_R96 && !W8) launch_mfma<CfgR96, false, EPI>(a, st, ev);
     else if (cfg == C_QL) launch_mfma<QL, W8, EPI>(a, st, ev);
     else launch_mfma<CfgS, W8, EPI>(a, st, ev);
   }
@@ -366,6 +383,7 @@ phi_status norm(bool embed, NormArgs a, hipStream_t st, const hipEvent_t* ev = n
     if (embed) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, true, CH>), dim3(a.T), dim3(kNormThreads), st, a);       \
     else if (a.nsplit == 0) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH, 0>), dim3(a.T), dim3(kNormThreads), st, a); \
     else if (a.nsplit == 5) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH, 5>), dim3(a.T), dim3(kNormThreads), st, a); \
+    else if (a.nsplit == 4) PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH, 4>), dim3(a.T), dim3(kNormThreads), st, a); \
     else PHI_LAUNCH(ev, (phi_norm_kernel<ET, AT, false, CH>), dim3(a.T), dim3(kNormThreads), st, a);            \
     break;
     PHI_NORM_CASE(1) PHI_NORM_CASE(2) PHI_NORM_CASE(3) PHI_NORM_CASE(4)
