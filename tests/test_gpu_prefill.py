@@ -211,6 +211,23 @@ def test_mini_w8_one_layer_ragged_1100_vs_oracle(phi):
     _gate(got, ref)
 
 
+@pytest.mark.parametrize("batch,seq", [(1, 300), (3, 101)])
+def test_mini_w8_one_layer_under_1024_vs_oracle(phi, batch, seq):
+    """Full Phi-3-mini width, one layer, int8 weights, under 1024 tokens,
+    against the oracle on those weights: the int8 128 x 192 QKV tile, the
+    5-split residual GEMMs on 256 x 128 tiles (binary16 partials summed by the
+    RMSNorm), the int8 256 x 128 gate/up tile and the 256 x 256 lm_head, with
+    a ragged last M-tile (and, at S = 101, sequences that straddle tiles)."""
+    from logits_parity_amd.weights import to_device
+    cfg = replace(synth.MINI_W8, n_layers=1)
+    _say(f"mini int8 1 layer {batch}x{seq}")
+    ws = synth.WeightSet(cfg)
+    ids = synth.token_ids(cfg, batch, seq)
+    got = _run(phi, cfg, to_device(ws, 1, "cuda"), ids)
+    ref = prefill.prefill_logits(cfg, ws, ids)
+    _gate(got, ref)
+
+
 @pytest.mark.parametrize("wtype", ["f16", "i8"])
 def test_mini_one_layer_ragged_4000_vs_oracle(phi, wtype):
     """One layer, 4000 tokens: the residual GEMMs take the 8-wave 256 x 192
